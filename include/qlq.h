@@ -1,0 +1,168 @@
+/*
+ * qlq.h -- C ABI of the MI355X (gfx950) quantized linear layer library (libqlq.so).
+ *
+ * The operations are the ones the pages describe for a quantized nn.Linear in an
+ * LLM serving engine:
+ *  - "Nano-vLLM-MoE" README (GitHub), section "FP8 W8A16 weight-only quantization"
+ *    (Setup: FP8 weights dequantized to BF16 inside the GEMM, bf16 x bf16 dot with
+ *    fp32 accumulation, bf16 out) and section "FP8 W8A8 static quantization"
+ *    (offline-calibrated activation scales; a scaled FP8 GEMM with a custom epilogue).
+ *  - "Nano-vLLM-MOE" README mirror, section "INT8 量化支持" (INT8 quantization
+ *    support): scheme table (int8_w8a16, int8_w8a8_static) and key-design list
+ *    (W8A16 dequantizes int8 weights to BF16 for a standard matmul; W8A8 static
+ *    quantizes activations with one fixed, offline-calibrated scalar per layer and
+ *    runs an INT8 GEMM with int32 accumulation).
+ *
+ * Notation: x is [M, K] (tokens x in-features), W is [N, K] (out x in), y = x W^T is
+ * [M, N]; every matrix is row-major and densely packed (row stride = its column count).
+ *
+ * Conventions common to every call:
+ *  - Pointers are DEVICE pointers (memory of the current HIP device) unless stated.
+ *    The caller owns every buffer; the library never allocates, frees or
+ *    synchronizes inside these calls.
+ *  - Calls are asynchronous: they validate their arguments on the host, enqueue
+ *    kernels on `stream` (0 = the null stream) and return.  A kernel fault shows
+ *    up at the caller's next synchronization.  Nothing here blocks the host, so
+ *    the calls may be recorded into a HIP graph.
+ *  - Errors: QLQ_ERR_INVALID_ARG for a null pointer where one is required, a size
+ *    below 1, a non-finite or non-positive scale, a scale count that is neither 1
+ *    nor N, or a workspace that is too small; QLQ_ERR_UNSUPPORTED for an enum value
+ *    the call does not know; QLQ_ERR_HIP when a launch fails.  On error nothing is
+ *    enqueued and qlq_last_error() returns a message (thread-local).
+ *  - Numbers: bf16 and OCP FP8 e4m3fn (1-4-3, bias 7, max 448, no infinities;
+ *    not the "fnuz" variant).  Non-finite inputs are not supported.
+ */
+#ifndef QLQ_H_
+#define QLQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLQ_OK = 0,
+  QLQ_ERR_INVALID_ARG = 1,
+  QLQ_ERR_UNSUPPORTED = 2,
+  QLQ_ERR_HIP = 3
+} qlq_status;
+
+/* Code type of quantized weights and activations. */
+typedef enum {
+  QLQ_INT8 = 0,        /* signed 8-bit integer codes in [-127, 127], qmax = 127 */
+  QLQ_FP8_E4M3FN = 1   /* OCP e4m3fn codes, qmax = 448 */
+} qlq_qtype;
+
+/* Weight scale granularity. */
+typedef enum {
+  QLQ_PER_CHANNEL = 0, /* one fp32 scale per output channel n: w_scale[N] */
+  QLQ_PER_TENSOR = 1   /* one fp32 scale for the whole matrix: w_scale[1] */
+} qlq_granularity;
+
+/* Output of qlq_qlinear_w8a8_static. */
+typedef enum {
+  QLQ_OUT_BF16 = 0,    /* y bf16 [M, N] after the scale epilogue */
+  QLQ_OUT_ACC = 1      /* raw accumulators, no epilogue: int32 [M, N] for INT8,
+                          fp32 [M, N] for FP8 */
+} qlq_out;
+
+/* Which GEMM a workspace is sized for. */
+typedef enum {
+  QLQ_SCHEME_W8A16 = 0,
+  QLQ_SCHEME_W8A8_STATIC = 1
+} qlq_scheme;
+
+/* ------------------------------------------------------------------ sizing */
+
+/* Bytes of the packed weight buffer for an [N, K] weight: N and K are rounded up
+ * to the tile grid (16 output channels x 64 inputs, 1 KiB per tile).  About N*K,
+ * i.e. half of the bf16 weight ("~0.5GB (-50%)" in the INT8 performance table of
+ * the "Nano-vLLM-MOE" mirror).  Returns 0 for N or K below 1. */
+size_t qlq_packed_weight_bytes(int64_t N, int64_t K);
+
+/* Bytes of workspace a GEMM call with these sizes needs (0 when the call needs
+ * none).  The workspace holds split-K partial sums and arrival counters.  It must
+ * be zero-filled before its first use; every completed call leaves the counters
+ * at zero again, so one buffer can serve every later call on the same stream.
+ * Calls that overlap in time (different streams) need separate workspaces. */
+size_t qlq_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype);
+
+/* ------------------------------------------------------------------ weights */
+
+/* Symmetric weight quantization and packing ("--scheme fp8_w8a16 / int8_w8a16 /
+ * *_w8a8_static" export step of both nano-vllm-moe READMEs).
+ *   w          [N, K] row-major, fp32 (w_is_bf16 = 0) or bf16 (w_is_bf16 = 1)
+ *   scale      per channel: s[n] = absmax_k |w[n,k]| / qmax; per tensor: one s over
+ *              all of W; fp32, correctly rounded division; an all-zero row
+ *              (tensor) gets s = 1
+ *   codes      q = round-to-nearest-even(w / s) (IEEE fp32 division), clamped to
+ *              +-127 (INT8) or saturated to +-448 (e4m3fn)
+ *   wq_packed  out, qlq_packed_weight_bytes(N, K) bytes, tiled layout private to
+ *              the library (pad entries are code 0); 256-byte aligned
+ *   w_scale    out, fp32 [N] (per channel) or [1] (per tensor)
+ * Per tensor, the call runs a reduction before the packing kernel; both are
+ * enqueued on `stream`. */
+qlq_status qlq_quantize_weight(const void* w, int w_is_bf16, int64_t N, int64_t K,
+                               qlq_qtype qtype, qlq_granularity granularity,
+                               void* wq_packed, float* w_scale, hipStream_t stream);
+
+/* Test hook: unpacks wq_packed into row-major 1-byte codes wq_rowmajor [N, K]. */
+qlq_status qlq_unpack_weight(const void* wq_packed, int64_t N, int64_t K,
+                             void* wq_rowmajor, hipStream_t stream);
+
+/* --------------------------------------------------------------- activations */
+
+/* Offline static calibration (the "--calib-samples 64 --calib-seqlen 512" step of
+ * the INT8 section of the "Nano-vLLM-MOE" mirror): input_scale_out[0] =
+ * absmax(x_calib) / qmax in fp32 (1 if x_calib is all zero).  x_calib is bf16 with
+ * `numel` elements; input_scale_out is a device float. */
+qlq_status qlq_calibrate_input_scale(const void* x_calib_bf16, int64_t numel, qlq_qtype qtype,
+                                     float* input_scale_out, hipStream_t stream);
+
+/* Static activation quantization with one fixed fp32 scalar (key-design list of
+ * the INT8 section: no per-token reduction at run time):
+ *   xq[m,k] = sat(round-to-nearest-even(x[m,k] / input_scale))
+ * x bf16 [M, K]; xq [M, K] one byte per code; input_scale is a host value. */
+qlq_status qlq_quantize_act_static(const void* x_bf16, int64_t M, int64_t K, float input_scale,
+                                   qlq_qtype qtype, void* xq, hipStream_t stream);
+
+/* -------------------------------------------------------------------- GEMMs */
+
+/* Weight-only quantized linear (W8A16):
+ *   y[m,n] = bf16( sum_k x[m,k] * bf16(fp32(q[n,k]) * s[n]) ), fp32 accumulation.
+ * x bf16 [M, K]; wq_packed/w_scale from qlq_quantize_weight with the same N, K and
+ * qtype; w_scale_numel is 1 (per tensor) or N (per channel); y bf16 [M, N].
+ * workspace may be NULL when qlq_workspace_bytes(QLQ_SCHEME_W8A16, ...) is 0. */
+qlq_status qlq_qlinear_w8a16(const void* x_bf16, int64_t M, int64_t K, int64_t N,
+                             const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                             qlq_qtype qtype, void* y_bf16,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* W8A8 static quantized linear on codes from qlq_quantize_act_static:
+ *   acc[m,n] = sum_k xq[m,k] * q[n,k]   (INT8: exact int32; FP8: fp32)
+ *   y[m,n]   = bf16( fp32(acc[m,n]) * fp32(input_scale * s[n]) )
+ * out = QLQ_OUT_ACC writes acc itself (int32 or fp32 [M, N]) to y instead.
+ * INT8 requires K <= 133144 so that |acc| < 2^31. */
+qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale,
+                                   int64_t M, int64_t K, int64_t N,
+                                   const void* wq_packed, const float* w_scale,
+                                   int64_t w_scale_numel, qlq_qtype qtype, qlq_out out,
+                                   void* y, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------- errors */
+
+const char* qlq_status_string(qlq_status status);
+const char* qlq_last_error(void);
+
+/* Library version string, e.g. "qlq 0.1.0 gfx950". */
+const char* qlq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLQ_H_ */

@@ -1,0 +1,116 @@
+"""The C ABI library loads, exports what include/qlq.h declares, and validates
+its arguments on the host (CPU only: every call here is rejected before any
+kernel is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_quantized_linear_qlinear_amd as qlq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlq.h")
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = _declared()
+    for n in ["qlq_quantize_weight", "qlq_qlinear_w8a16", "qlq_quantize_act_static", "qlq_qlinear_w8a8_static",
+              "qlq_calibrate_input_scale", "qlq_unpack_weight", "qlq_packed_weight_bytes",
+              "qlq_workspace_bytes", "qlq_status_string", "qlq_last_error", "qlq_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(qlq.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_signatures_cover_the_header():
+    from weight_quantized_linear_qlinear_amd import binding
+    assert sorted(binding._SIGNATURES) == _declared()
+
+
+def test_version_and_status_strings():
+    L = qlq.lib()
+    assert L.qlq_version().decode().startswith("qlq")
+    assert [L.qlq_status_string(i).decode() for i in range(4)] == \
+        ["QLQ_OK", "QLQ_ERR_INVALID_ARG", "QLQ_ERR_UNSUPPORTED", "QLQ_ERR_HIP"]
+
+
+def test_packed_bytes_is_tile_padded_and_about_half_of_bf16():
+    assert qlq.packed_weight_bytes(16, 64) == 1024
+    assert qlq.packed_weight_bytes(1, 1) == 1024
+    assert qlq.packed_weight_bytes(17, 65) == 32 * 128
+    assert qlq.packed_weight_bytes(0, 5) == 0
+    # INT8 table of the Nano-vLLM-MOE mirror: weight memory ~0.5x of BF16
+    for N, K in [(2048, 2048), (11008, 2048), (2048, 11008)]:
+        assert qlq.packed_weight_bytes(N, K) == N * K == (2 * N * K) // 2
+
+
+def test_workspace_sizes():
+    assert qlq.workspace_bytes("w8a16", 16, 2048, 11008, "fp8_e4m3fn") == 0      # enough column blocks
+    assert qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8") > 0               # split over K
+    assert qlq.workspace_bytes("w8a8_static", 1024, 2048, 11008, "fp8_e4m3fn") == 0
+    assert qlq.workspace_bytes("w8a8_static", 256, 11008, 2048, "int8") > 0
+    assert qlq.workspace_bytes("w8a16", 0, 64, 64, "int8") == 0
+
+
+def _status(fn, *args):
+    return fn(*args), qlq.lib().qlq_last_error().decode()
+
+
+def test_validation_null_pointers_and_sizes():
+    L = qlq.lib()
+    st, msg = _status(L.qlq_qlinear_w8a16, None, 1, 64, 16, FAKE, FAKE, 16, 0, FAKE, None, 0, None)
+    assert st == 1 and "null" in msg
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 0, 64, 16, FAKE, FAKE, 16, 0, FAKE, None, 0, None)
+    assert st == 1 and ">= 1" in msg
+    st, _ = _status(L.qlq_quantize_weight, FAKE, 0, 16, -1, 0, 0, FAKE, FAKE, None)
+    assert st == 1
+    st, _ = _status(L.qlq_calibrate_input_scale, FAKE, 0, 0, FAKE, None)
+    assert st == 1
+
+
+def test_validation_enums_scales_and_workspace():
+    L = qlq.lib()
+    st, _ = _status(L.qlq_qlinear_w8a16, FAKE, 1, 64, 16, FAKE, FAKE, 16, 7, FAKE, None, 0, None)
+    assert st == 2
+    st, _ = _status(L.qlq_quantize_weight, FAKE, 0, 16, 64, 0, 5, FAKE, FAKE, None)
+    assert st == 2
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 64, 16, FAKE, FAKE, 3, 0, FAKE, None, 0, None)
+    assert st == 1 and "w_scale_numel" in msg
+    for bad in [0.0, -1.0, float("inf"), float("nan")]:
+        st, msg = _status(L.qlq_quantize_act_static, FAKE, 4, 64, bad, 0, FAKE, None)
+        assert st == 1 and "input_scale" in msg
+        st, _ = _status(L.qlq_qlinear_w8a8_static, FAKE, bad, 4, 64, 16, FAKE, FAKE, 16, 0, 0, FAKE, None, 0, None)
+        assert st == 1
+    st, _ = _status(L.qlq_qlinear_w8a8_static, FAKE, 1.0, 4, 64, 16, FAKE, FAKE, 16, 0, 9, FAKE, None, 0, None)
+    assert st == 2
+    # INT8 accumulator bound: K <= 133144
+    st, msg = _status(L.qlq_qlinear_w8a8_static, FAKE, 1.0, 4, 133145, 16, FAKE, FAKE, 16, 0, 0, FAKE, None, 0, None)
+    assert st == 1 and "133144" in msg
+    # a split-K plan needs its workspace
+    need = qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8")
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 2048, FAKE, FAKE, 2048, 0, FAKE, None, 0, None)
+    assert st == 1 and "workspace" in msg
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 2048, FAKE, FAKE, 2048, 0, FAKE, FAKE, need - 1, None)
+    assert st == 1 and "workspace" in msg
+    # misaligned packed weights
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 64, 16, ctypes.c_void_p(0x10008), FAKE, 16, 0, FAKE, None, 0,
+                      None)
+    assert st == 1 and "aligned" in msg
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        qlq.quantize_weight(torch.zeros(4, 4), "int8")

@@ -1,0 +1,238 @@
+"""ctypes binding of libqlq.so: argument marshalling only.
+
+Every function here checks shapes and dtypes, allocates outputs with PyTorch on
+the tensors' device, and forwards plain pointers, sizes and the current HIP
+stream to the C ABI declared in include/qlq.h.  All arithmetic runs in the HIP
+kernels; there is no fallback path: if the library is not built, or the tensors
+are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlq.so")
+
+QTYPES = {"int8": 0, "fp8_e4m3fn": 1}
+GRANULARITIES = {"per_channel": 0, "per_tensor": 1}
+OUTS = {"bf16": 0, "acc": 1}
+SCHEMES = {"w8a16": 0, "w8a8_static": 1}
+STATUS = {0: "QLQ_OK", 1: "QLQ_ERR_INVALID_ARG", 2: "QLQ_ERR_UNSUPPORTED", 3: "QLQ_ERR_HIP"}
+
+# name -> (restype, argtypes), mirroring include/qlq.h
+_c = ctypes
+_SIGNATURES = {
+    "qlq_packed_weight_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64]),
+    "qlq_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "qlq_quantize_weight": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
+                                       _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "qlq_unpack_weight": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p]),
+    "qlq_calibrate_input_scale": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p]),
+    "qlq_quantize_act_static": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_float, _c.c_int,
+                                           _c.c_void_p, _c.c_void_p]),
+    "qlq_qlinear_w8a16": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                                     _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_qlinear_w8a8_static": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
+                                           _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
+                                           _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_status_string": (_c.c_char_p, [_c.c_int]),
+    "qlq_last_error": (_c.c_char_p, []),
+    "qlq_version": (_c.c_char_p, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class QlqError(RuntimeError):
+    """A non-OK status from libqlq (validation or launch failure)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libqlq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                                      "`python -m weight_quantized_linear_qlinear_amd.build`")
+                h = ctypes.CDLL(_LIB_PATH)
+                for name, (res, args) in _SIGNATURES.items():
+                    f = getattr(h, name)
+                    f.restype = res
+                    f.argtypes = args
+                _lib = h
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise QlqError(status, lib().qlq_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require_gpu(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("qlq operates on GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("qlq needs contiguous (row-major) tensors")
+
+
+def _qtype(q: str) -> int:
+    if q not in QTYPES:
+        raise ValueError(f"qtype must be one of {sorted(QTYPES)}")
+    return QTYPES[q]
+
+
+def code_dtype(qtype: str) -> torch.dtype:
+    """torch dtype used for 1-byte codes: int8 for INT8, uint8 (raw bits) for e4m3fn."""
+    return torch.int8 if qtype == "int8" else torch.uint8
+
+
+# ---------------------------------------------------------------------- sizing
+def packed_weight_bytes(N: int, K: int) -> int:
+    return int(lib().qlq_packed_weight_bytes(N, K))
+
+
+def workspace_bytes(scheme: str, M: int, K: int, N: int, qtype: str) -> int:
+    return int(lib().qlq_workspace_bytes(SCHEMES[scheme], M, K, N, _qtype(qtype)))
+
+
+_workspaces: dict = {}
+
+
+def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor | None:
+    """A zero-filled per-device workspace, grown on demand (the kernels leave it zeroed)."""
+    if nbytes == 0:
+        return None
+    key = (dev.type, dev.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------- weights
+@dataclasses.dataclass
+class QuantizedWeight:
+    """A packed quantized weight of logical shape [N, K] and its fp32 scales."""
+    packed: torch.Tensor      # uint8, packed_weight_bytes(N, K)
+    scale: torch.Tensor       # fp32 [N] (per channel) or [1] (per tensor)
+    N: int
+    K: int
+    qtype: str
+    granularity: str
+
+
+def quantize_weight(w: torch.Tensor, qtype: str, granularity: str = "per_channel",
+                    packed: torch.Tensor | None = None, scale: torch.Tensor | None = None) -> QuantizedWeight:
+    """Quantize and pack W[N, K] (fp32 or bf16, on the GPU)."""
+    _require_gpu(w)
+    if w.dim() != 2 or w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be a 2-D fp32 or bf16 tensor")
+    N, K = w.shape
+    if granularity not in GRANULARITIES:
+        raise ValueError(f"granularity must be one of {sorted(GRANULARITIES)}")
+    if packed is None:
+        packed = torch.empty(packed_weight_bytes(N, K), dtype=torch.uint8, device=w.device)
+    if scale is None:
+        scale = torch.empty(N if granularity == "per_channel" else 1, dtype=torch.float32, device=w.device)
+    _check(lib().qlq_quantize_weight(_ptr(w), int(w.dtype == torch.bfloat16), N, K, _qtype(qtype),
+                                     GRANULARITIES[granularity], _ptr(packed), _ptr(scale), _stream(w.device)))
+    return QuantizedWeight(packed, scale, N, K, qtype, granularity)
+
+
+def unpack_weight(qw: QuantizedWeight) -> torch.Tensor:
+    """Row-major [N, K] codes of a packed weight (test hook)."""
+    out = torch.empty((qw.N, qw.K), dtype=code_dtype(qw.qtype), device=qw.packed.device)
+    _check(lib().qlq_unpack_weight(_ptr(qw.packed), qw.N, qw.K, _ptr(out), _stream(out.device)))
+    return out
+
+
+# ---------------------------------------------------------------------- activations
+def calibrate_input_scale(x_calib: torch.Tensor, qtype: str, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Static input scale absmax(x_calib) / qmax as a one-element fp32 device tensor."""
+    _require_gpu(x_calib)
+    if x_calib.dtype != torch.bfloat16:
+        raise ValueError("x_calib must be bf16")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x_calib.device)
+    _check(lib().qlq_calibrate_input_scale(_ptr(x_calib), x_calib.numel(), _qtype(qtype), _ptr(out),
+                                           _stream(x_calib.device)))
+    return out
+
+
+def quantize_act_static(x: torch.Tensor, input_scale: float, qtype: str,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Codes of x [M, K] bf16 with the fixed scalar input_scale."""
+    _require_gpu(x)
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=code_dtype(qtype), device=x.device)
+    _check(lib().qlq_quantize_act_static(_ptr(x), M, K, float(input_scale), _qtype(qtype), _ptr(out),
+                                         _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------------- GEMMs
+def qlinear_w8a16(x: torch.Tensor, qw: QuantizedWeight, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x W^T with W dequantized to bf16 in the kernel; x bf16 [M, K] -> y bf16 [M, N]."""
+    _require_gpu(x)
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.shape[1] != qw.K:
+        raise ValueError(f"x must be bf16 [M, {qw.K}]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, qw.N), dtype=torch.bfloat16, device=x.device)
+    nbytes = workspace_bytes("w8a16", M, qw.K, qw.N, qw.qtype)
+    ws = workspace if workspace is not None else _workspace(x.device, nbytes)
+    _check(lib().qlq_qlinear_w8a16(_ptr(x), M, qw.K, qw.N, _ptr(qw.packed), _ptr(qw.scale), qw.scale.numel(),
+                                   _qtype(qw.qtype), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(x.device)))
+    return out
+
+
+def qlinear_w8a8_static(xq: torch.Tensor, input_scale: float, qw: QuantizedWeight, out_mode: str = "bf16",
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W8A8 static GEMM on codes xq [M, K]: bf16 y [M, N], or raw accumulators (out_mode="acc")."""
+    _require_gpu(xq)
+    if xq.dim() != 2 or xq.element_size() != 1 or xq.shape[1] != qw.K:
+        raise ValueError(f"xq must be 1-byte codes [M, {qw.K}]")
+    M = xq.shape[0]
+    if out is None:
+        if out_mode == "acc":
+            dt = torch.int32 if qw.qtype == "int8" else torch.float32
+        else:
+            dt = torch.bfloat16
+        out = torch.empty((M, qw.N), dtype=dt, device=xq.device)
+    nbytes = workspace_bytes("w8a8_static", M, qw.K, qw.N, qw.qtype)
+    ws = workspace if workspace is not None else _workspace(xq.device, nbytes)
+    _check(lib().qlq_qlinear_w8a8_static(_ptr(xq), float(input_scale), M, qw.K, qw.N, _ptr(qw.packed),
+                                         _ptr(qw.scale), qw.scale.numel(), _qtype(qw.qtype), OUTS[out_mode],
+                                         _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                         _stream(xq.device)))
+    return out

@@ -1,0 +1,260 @@
+// C ABI of libqlq.so: argument validation, kernel-family choice and launch.
+// Declarations and their contracts: include/qlq.h.
+#include "qlq.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "qlq_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qlq_status fail(qlq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+qlq_status fail(qlq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+qlq_status ok() {
+  g_last_error.clear();
+  return QLQ_OK;
+}
+
+qlq_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QLQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;        // keeps every in-kernel index in range
+constexpr int64_t kMaxInt8K = 133144;                // 127 * 127 * K < 2^31
+// Split-K workspaces start with one fixed-size counter region shared by every
+// plan, so partial sums of one call never land on counters of another.
+constexpr int64_t kMaxSplitTiles = 1024;
+constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+qlq_status check_dims(int64_t M, int64_t K, int64_t N) {
+  if (M < 1 || K < 1 || N < 1) return fail(QLQ_ERR_INVALID_ARG, "sizes must be >= 1 (M=%lld K=%lld N=%lld)",
+                                           (long long)M, (long long)K, (long long)N);
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim)
+    return fail(QLQ_ERR_INVALID_ARG, "sizes above 2^24 are not supported");
+  return QLQ_OK;
+}
+
+qlq_status check_qtype(qlq_qtype q) {
+  if (q != QLQ_INT8 && q != QLQ_FP8_E4M3FN) return fail(QLQ_ERR_UNSUPPORTED, "unknown qtype %d", (int)q);
+  return QLQ_OK;
+}
+
+qlq_status check_scale(float s, const char* name) {
+  if (!std::isfinite(s) || !(s > 0.0f)) return fail(QLQ_ERR_INVALID_ARG, "%s must be finite and > 0", name);
+  return QLQ_OK;
+}
+
+}  // namespace
+
+namespace qlq {
+
+GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N) {
+  GemmPlan p;
+  const int64_t KT = cdiv(K, 64), NT = cdiv(N, 16);
+  if (M <= 16) {
+    // Small-M: one workgroup per 16 output columns and K slice; enough
+    // workgroups to cover the 256 CUs about twice.
+    p.kind = 0;
+    const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
+    const int64_t KU = cdiv(KT, TPU);
+    int64_t S = 1;
+    if (NT < 512) {   // NT < 512 <= kMaxSplitTiles
+      S = cdiv(512, NT);
+      int64_t cap = KU / 4 > 1 ? KU / 4 : 1;
+      if (S > cap) S = cap;
+    }
+    const int64_t ups = cdiv(KU, S);
+    S = cdiv(KU, ups);
+    p.S = (int)S;
+    p.units_per_split = (int)ups;
+    p.units_per_wave = (int)cdiv(ups, 4);
+    p.tiles = (int)NT;
+    p.grid = (int)(NT * S);
+    if (S > 1) {
+      p.ws_counter_bytes = kCounterBytes;
+      p.ws_bytes = p.ws_counter_bytes + (size_t)S * NT * 64 * 16;
+    }
+  } else {
+    p.kind = 1;
+    p.BM = 128;
+    p.BN = 128;
+    const int64_t tiles = cdiv(M, p.BM) * cdiv(N, p.BN);
+    const int64_t BKT = scheme == kW8A16 ? 1 : 2;
+    const int64_t KU = cdiv(KT, BKT);
+    int64_t S = 1;
+    if (tiles < 240) {   // 240 <= kMaxSplitTiles
+      S = cdiv(256, tiles);
+      int64_t cap = KU / 4 > 1 ? KU / 4 : 1;
+      if (S > cap) S = cap;
+    }
+    const int64_t ups = cdiv(KU, S);
+    S = cdiv(KU, ups);
+    p.S = (int)S;
+    p.units_per_split = (int)ups;
+    p.tiles = (int)tiles;
+    p.grid = (int)(tiles * S);
+    if (S > 1) {
+      const int64_t nv = (p.BM / 32) * (p.BN / 32);   // f32x4 values per thread
+      p.ws_counter_bytes = kCounterBytes;
+      p.ws_bytes = p.ws_counter_bytes + (size_t)S * tiles * nv * 256 * 16;
+    }
+  }
+  return p;
+}
+
+}  // namespace qlq
+
+extern "C" {
+
+const char* qlq_status_string(qlq_status s) {
+  switch (s) {
+    case QLQ_OK: return "QLQ_OK";
+    case QLQ_ERR_INVALID_ARG: return "QLQ_ERR_INVALID_ARG";
+    case QLQ_ERR_UNSUPPORTED: return "QLQ_ERR_UNSUPPORTED";
+    case QLQ_ERR_HIP: return "QLQ_ERR_HIP";
+  }
+  return "QLQ_UNKNOWN_STATUS";
+}
+
+const char* qlq_last_error(void) { return g_last_error.c_str(); }
+
+const char* qlq_version(void) { return "qlq 0.1.0 gfx950"; }
+
+size_t qlq_packed_weight_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K, 64) * 64;
+}
+
+size_t qlq_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype) {
+  if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
+  if (scheme != QLQ_SCHEME_W8A16 && scheme != QLQ_SCHEME_W8A8_STATIC) return 0;
+  return qlq::plan_gemm((int)scheme, (int)qtype, M, K, N).ws_bytes;
+}
+
+qlq_status qlq_quantize_weight(const void* w, int w_is_bf16, int64_t N, int64_t K, qlq_qtype qtype,
+                               qlq_granularity granularity, void* wq_packed, float* w_scale,
+                               hipStream_t stream) {
+  if (!w || !wq_packed || !w_scale) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(1, K, N)) return st;
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (granularity != QLQ_PER_CHANNEL && granularity != QLQ_PER_TENSOR)
+    return fail(QLQ_ERR_UNSUPPORTED, "unknown granularity %d", (int)granularity);
+  if (!aligned(wq_packed, 16)) return fail(QLQ_ERR_INVALID_ARG, "wq_packed must be 16-byte aligned");
+  if (!aligned(w, w_is_bf16 ? 2 : 4) || !aligned(w_scale, 4)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(qlq::launch_pack_weight(w, w_is_bf16 ? 1 : 0, (int)N, (int)K, (int)qtype,
+                                            granularity == QLQ_PER_TENSOR, static_cast<uint8_t*>(wq_packed),
+                                            w_scale, stream),
+                    "quantize_weight");
+}
+
+qlq_status qlq_unpack_weight(const void* wq_packed, int64_t N, int64_t K, void* wq_rowmajor, hipStream_t stream) {
+  if (!wq_packed || !wq_rowmajor) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(1, K, N)) return st;
+  return hip_status(qlq::launch_unpack_weight(static_cast<const uint8_t*>(wq_packed), (int)N, (int)K,
+                                              static_cast<uint8_t*>(wq_rowmajor), stream),
+                    "unpack_weight");
+}
+
+qlq_status qlq_calibrate_input_scale(const void* x_calib_bf16, int64_t numel, qlq_qtype qtype,
+                                     float* input_scale_out, hipStream_t stream) {
+  if (!x_calib_bf16 || !input_scale_out) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (numel < 1) return fail(QLQ_ERR_INVALID_ARG, "numel must be >= 1");
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (!aligned(x_calib_bf16, 2) || !aligned(input_scale_out, 4)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(qlq::launch_absmax_scale(x_calib_bf16, 1, numel, qtype == QLQ_FP8_E4M3FN ? 448.0f : 127.0f,
+                                             input_scale_out, stream),
+                    "calibrate_input_scale");
+}
+
+qlq_status qlq_quantize_act_static(const void* x_bf16, int64_t M, int64_t K, float input_scale, qlq_qtype qtype,
+                                   void* xq, hipStream_t stream) {
+  if (!x_bf16 || !xq) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(M, K, 1)) return st;
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (qlq_status st = check_scale(input_scale, "input_scale")) return st;
+  if (!aligned(x_bf16, 2)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream),
+                    "quantize_act_static");
+}
+
+static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int64_t N, const void* wq_packed,
+                           const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
+                           int out_acc, void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(M, K, N)) return st;
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (w_scale_numel != 1 && w_scale_numel != N)
+    return fail(QLQ_ERR_INVALID_ARG, "w_scale_numel must be 1 or N (got %lld, N=%lld)", (long long)w_scale_numel,
+                (long long)N);
+  if (!aligned(wq_packed, 16)) return fail(QLQ_ERR_INVALID_ARG, "wq_packed must be 16-byte aligned");
+  if (!aligned(w_scale, 4) || !aligned(y, 4) || !aligned(x, scheme == qlq::kW8A16 ? 2 : 1))
+    return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  qlq::GemmPlan plan = qlq::plan_gemm(scheme, (int)qtype, M, K, N);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(QLQ_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", plan.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  qlq::GemmArgs a;
+  a.x = x;
+  a.w = static_cast<const uint8_t*>(wq_packed);
+  a.w_scale = w_scale;
+  a.scale_per_tensor = w_scale_numel == 1 ? 1 : 0;
+  a.y = y;
+  a.counters = plan.ws_bytes ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.partials = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_counter_bytes)
+                             : nullptr;
+  a.M = (int)M;
+  a.K = (int)K;
+  a.N = (int)N;
+  a.KT = (int)cdiv(K, 64);
+  a.NT = (int)cdiv(N, 16);
+  a.input_scale = input_scale;
+  a.out_acc = out_acc;
+  a.fast = (K % 64 == 0) && aligned(x, 16);
+  hipError_t e = plan.kind == 0 ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
+                                : qlq::launch_gemm_large(scheme, (int)qtype, plan, a, stream);
+  return hip_status(e, scheme == qlq::kW8A16 ? "qlinear_w8a16" : "qlinear_w8a8_static");
+}
+
+qlq_status qlq_qlinear_w8a16(const void* x_bf16, int64_t M, int64_t K, int64_t N, const void* wq_packed,
+                             const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, void* y_bf16,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_gemm(qlq::kW8A16, x_bf16, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, 1.0f, 0, y_bf16,
+                  workspace, workspace_bytes, stream);
+}
+
+qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale, int64_t M, int64_t K, int64_t N,
+                                   const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                                   qlq_qtype qtype, qlq_out out, void* y, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (qlq_status st = check_scale(input_scale, "input_scale")) return st;
+  if (out != QLQ_OUT_BF16 && out != QLQ_OUT_ACC) return fail(QLQ_ERR_UNSUPPORTED, "unknown out mode %d", (int)out);
+  if (qtype == QLQ_INT8 && K > kMaxInt8K)
+    return fail(QLQ_ERR_INVALID_ARG, "INT8 W8A8 needs K <= %lld for an exact int32 accumulator",
+                (long long)kMaxInt8K);
+  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale,
+                  out == QLQ_OUT_ACC ? 1 : 0, y, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

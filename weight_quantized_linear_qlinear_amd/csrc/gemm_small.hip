@@ -1,0 +1,218 @@
+// Small-M (decode, M <= 16) quantized GEMM family.
+//
+// Decode is bound by reading the weights once ("Nano-vLLM-MoE" README, section
+// "FP8 W8A16 weight-only quantization", Analysis: the FP8->BF16 dequant GEMM trades
+// weight bandwidth for compute; "Nano-vLLM-MOE" mirror, Llama 3.1 8B section:
+// decode leans on weight bandwidth).  So every weight byte is loaded exactly once
+// with 16-byte coalesced loads (a wave reads one contiguous KiB tile), issued in
+// batches before any arithmetic, and the arithmetic runs on the matrix cores:
+//   W8A16: codes -> bf16(fp32(q) * s[n]) in registers -> v_mfma_f32_16x16x32_bf16
+//   W8A8 INT8: v_mfma_i32_16x16x64_i8 on the codes (exact int32)
+//   W8A8 FP8:  v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3) on the codes
+// M <= 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
+//
+// Work split: workgroup (nt, s) owns output columns [16 nt, 16 nt + 16) and the
+// s-th slice of K; its four waves take consecutive sub-slices.  The four wave
+// accumulators are summed through LDS; with S > 1 slices per column block the
+// partial sums go to the workspace and the last workgroup to arrive adds them
+// in slice order (deterministic) and runs the epilogue.
+#include "qlq_device.h"
+#include "qlq_launch.h"
+
+namespace qlq {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 8;
+
+template <int QT, int SCH>
+struct SmallTraits {
+  static constexpr int kTilesPerUnit = (SCH == kW8A8 && QT == kFp8) ? 2 : 1;
+  static constexpr bool kIntAcc = (SCH == kW8A8 && QT == kInt8);
+};
+
+// 16 bf16 activations x[m, k .. k+15] (generic path: bounds-checked per element).
+template <bool FAST>
+__device__ __forceinline__ void load_x_bf16x16(const uint16_t* row, int k, int K, u32x4& lo, u32x4& hi) {
+  if constexpr (FAST) {
+    lo = ld16(row + k);
+    hi = ld16(row + k + 8);
+  } else {
+    uint32_t v[8];
+    for (int e = 0; e < 8; ++e) {
+      uint32_t a = (k + 2 * e < K) ? row[k + 2 * e] : 0u;
+      uint32_t b = (k + 2 * e + 1 < K) ? row[k + 2 * e + 1] : 0u;
+      v[e] = a | (b << 16);
+    }
+    lo = (u32x4){v[0], v[1], v[2], v[3]};
+    hi = (u32x4){v[4], v[5], v[6], v[7]};
+  }
+}
+
+// 16 one-byte codes xq[m, k .. k+15].
+template <bool FAST>
+__device__ __forceinline__ u32x4 load_x_codes16(const uint8_t* row, int k, int K) {
+  if constexpr (FAST) {
+    return ld16(row + k);
+  } else {
+    uint32_t v[4];
+    for (int e = 0; e < 4; ++e) {
+      uint32_t d = 0;
+      for (int b = 0; b < 4; ++b) {
+        int kk = k + 4 * e + b;
+        d |= (kk < K ? (uint32_t)row[kk] : 0u) << (8 * b);
+      }
+      v[e] = d;
+    }
+    return (u32x4){v[0], v[1], v[2], v[3]};
+  }
+}
+
+template <int QT, int SCH, bool FAST>
+__global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int ups, int upw) {
+  using T = SmallTraits<QT, SCH>;
+  constexpr int TPU = T::kTilesPerUnit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nt = blockIdx.x % a.NT;
+  const int s = blockIdx.x / a.NT;
+  const int KU = (a.KT + TPU - 1) / TPU;
+  const int u_begin = s * ups + wave * upw;
+  int u_end = u_begin + upw;
+  if (u_end > (s + 1) * ups) u_end = (s + 1) * ups;
+  if (u_end > KU) u_end = KU;
+
+  const int r = lane & 15, g = lane >> 4;
+  const int n = nt * kTileN + r;
+  float sc = 0.0f;
+  if (SCH == kW8A16) sc = a.scale_per_tensor ? a.w_scale[0] : (n < a.N ? a.w_scale[n] : 0.0f);
+  const float sc_m128 = -128.0f * sc;
+
+  // Row m = r of the A operand; rows >= M contribute zeros.
+  const bool row_ok = r < a.M;
+  const uint8_t* wbase = a.w + (int64_t)nt * a.KT * kTileBytes + lane * 16;
+
+  f32x4 accf = {0.f, 0.f, 0.f, 0.f};
+  i32x4 acci = {0, 0, 0, 0};
+
+  for (int u0 = u_begin; u0 < u_end; u0 += kUnroll) {
+    u32x4 wv[kUnroll][TPU];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i)
+#pragma unroll
+      for (int t = 0; t < TPU; ++t) {
+        int kt = (u0 + i) * TPU + t;
+        wv[i][t] = (u0 + i < u_end && kt < a.KT) ? ld16_stream(wbase + (int64_t)kt * kTileBytes)
+                                                  : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int u = u0 + i;
+      if (u >= u_end) break;
+      if constexpr (SCH == kW8A16) {
+        u32x4 xlo = {0u, 0u, 0u, 0u}, xhi = {0u, 0u, 0u, 0u};
+        if (row_ok)
+          load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, u * kTileK + g * 16,
+                               a.K, xlo, xhi);
+        bf16x8 b0 = dequant8<QT>(wv[i][0].x, wv[i][0].y, sc, sc_m128);
+        bf16x8 b1 = dequant8<QT>(wv[i][0].z, wv[i][0].w, sc, sc_m128);
+        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xlo), b0, accf);
+        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xhi), b1, accf);
+      } else {
+        const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K;
+        if constexpr (QT == kInt8) {
+          u32x4 xa = {0u, 0u, 0u, 0u};
+          if (row_ok) xa = load_x_codes16<FAST>(xrow, u * kTileK + g * 16, a.K);
+          acci = mfma_i8_k64(xa, wv[i][0], acci);
+        } else {
+          u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+          if (row_ok) {
+            x0 = load_x_codes16<FAST>(xrow, (2 * u) * kTileK + g * 16, a.K);
+            if (2 * u + 1 < a.KT) x1 = load_x_codes16<FAST>(xrow, (2 * u + 1) * kTileK + g * 16, a.K);
+          }
+          accf = mfma_fp8_k128(x0, x1, wv[i][0], wv[i][1], accf);
+        }
+      }
+    }
+  }
+
+  // ---- sum the four waves through LDS (wave 0 finishes the job)
+  __shared__ f32x4 red[kWaves][64];
+  f32x4 mine = T::kIntAcc ? __builtin_bit_cast(f32x4, acci) : accf;
+  red[wave][lane] = mine;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 tot;
+  if constexpr (T::kIntAcc) {
+    i32x4 t = __builtin_bit_cast(i32x4, red[0][lane]);
+    for (int w = 1; w < kWaves; ++w) t += __builtin_bit_cast(i32x4, red[w][lane]);
+    tot = __builtin_bit_cast(f32x4, t);
+  } else {
+    tot = red[0][lane];
+    for (int w = 1; w < kWaves; ++w) tot += red[w][lane];
+  }
+
+  // ---- split-K: publish, count arrivals, last one sums the slices in order
+  if (S > 1) {
+    f32x4* part = reinterpret_cast<f32x4*>(a.partials);
+    part[((int64_t)s * a.NT + nt) * 64 + lane] = tot;
+    __threadfence();
+    uint32_t prev = 0;
+    if (lane == 0) prev = atomicAdd(&a.counters[nt], 1u);
+    prev = __shfl(prev, 0, 64);
+    if (prev != (uint32_t)(S - 1)) return;
+    __threadfence();
+    if constexpr (T::kIntAcc) {
+      i32x4 t = {0, 0, 0, 0};
+      for (int q = 0; q < S; ++q)
+        t += (q == s) ? __builtin_bit_cast(i32x4, tot)
+                      : __builtin_bit_cast(i32x4, __builtin_nontemporal_load(&part[((int64_t)q * a.NT + nt) * 64 + lane]));
+      tot = __builtin_bit_cast(f32x4, t);
+    } else {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < S; ++q)
+        t += (q == s) ? tot : __builtin_nontemporal_load(&part[((int64_t)q * a.NT + nt) * 64 + lane]);
+      tot = t;
+    }
+    if (lane == 0) a.counters[nt] = 0u;
+  }
+
+  // ---- epilogue: lane holds D[4g + j][r] = y[m = 4g + j, n]
+  if (n >= a.N) return;
+  float comb = 0.0f;
+  if (SCH == kW8A8 && !a.out_acc)
+    comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = 4 * g + j;
+    if (m >= a.M) break;
+    const int64_t o = (int64_t)m * a.N + n;
+    if constexpr (SCH == kW8A16) {
+      reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)tot[j];
+    } else if (a.out_acc) {
+      reinterpret_cast<float*>(a.y)[o] = tot[j];   // int32 bits or fp32
+    } else {
+      float v = T::kIntAcc ? (float)__builtin_bit_cast(i32x4, tot)[j] : tot[j];
+      reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
+    }
+  }
+}
+
+template <int QT, int SCH>
+hipError_t launch_small_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  if (a.fast)
+    gemm_small_kernel<QT, SCH, true><<<p.grid, 256, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  else
+    gemm_small_kernel<QT, SCH, false><<<p.grid, 256, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_small(int scheme, int qtype, const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  if (scheme == kW8A16)
+    return qtype == kFp8 ? launch_small_t<kFp8, kW8A16>(p, a, st) : launch_small_t<kInt8, kW8A16>(p, a, st);
+  return qtype == kFp8 ? launch_small_t<kFp8, kW8A8>(p, a, st) : launch_small_t<kInt8, kW8A8>(p, a, st);
+}
+
+}  // namespace qlq

@@ -1,0 +1,149 @@
+// Device-side building blocks shared by the qlq kernels (gfx950 only).
+//
+// Packed weight layout (the library's private format, written by the packer and
+// read by every GEMM kernel): W[N, K] codes are cut into tiles of 16 output
+// channels x 64 inputs, 1 KiB each.  Tile (nt, kt) lives at byte
+// (nt * KT + kt) * 1024, KT = ceil(K / 64).  Inside a tile, byte
+//     lane * 16 + i,   lane = (n % 16) + 16 * ((k % 64) / 16),   i = k % 16
+// holds W[n, k].  So one 16-byte load by lane `lane` of a wave64 returns 16
+// consecutive inputs of one output channel, a whole wave reads one contiguous
+// KiB, and that register is exactly the per-lane B operand of a 16x16 MFMA
+// (column n = lane % 16, k-group = lane / 16) for the int8 K=64 shape, half of
+// it for the fp8 K=128 shape, and two bf16 K=32 operands after dequantization.
+// Pad rows (n >= N) and pad inputs (k >= K) hold code 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlq {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileN = 16;
+constexpr int kTileK = 64;
+constexpr int kTileBytes = 1024;
+
+enum QType : int { kInt8 = 0, kFp8 = 1 };
+
+// ---------------------------------------------------------------- conversions
+
+// Two fp32 -> packed bf16x2 (round to nearest even: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
+// fp32 -> e4m3fn code, round to nearest even, saturating at +-448 (the clamp runs
+// first so the hardware convert never sees a value it would turn into NaN).
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
+  float c = __builtin_amdgcn_fmed3f(v, 448.0f, -448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// Four fp32 -> four e4m3fn codes packed in a dword (byte i = value i).
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4_sat(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, 448.0f, -448.0f);
+  b = __builtin_amdgcn_fmed3f(b, 448.0f, -448.0f);
+  c = __builtin_amdgcn_fmed3f(c, 448.0f, -448.0f);
+  d = __builtin_amdgcn_fmed3f(d, 448.0f, -448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// fp32 -> int8 code: round to nearest even, clamp to +-127.
+__device__ __forceinline__ uint32_t f32_to_i8_sat(float v) {
+  float r = __builtin_rintf(v);
+  r = __builtin_amdgcn_fmed3f(r, 127.0f, -127.0f);
+  return (uint32_t)((int)r) & 0xFFu;
+}
+
+// Dequantize 8 codes (two dwords) to 8 bf16 = bf16(fp32(q) * s), one fp32
+// rounding for the product and one for the bf16 cast.
+template <int QT>
+__device__ __forceinline__ bf16x8 dequant8(uint32_t d0, uint32_t d1, float s, float s_m128) {
+  u32x4 r;
+  if constexpr (QT == kFp8) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, true);
+    f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, false);
+    f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, true);
+    r.x = pack_bf16x2(a.x * s, a.y * s);
+    r.y = pack_bf16x2(b.x * s, b.y * s);
+    r.z = pack_bf16x2(c.x * s, c.y * s);
+    r.w = pack_bf16x2(d.x * s, d.y * s);
+  } else {
+    // Flip the sign bit of every byte: u = q + 128 in [1, 255] converts with
+    // v_cvt_f32_ubyteN; then fma(u, s, -128 s) = q * s with a single rounding
+    // (-128 s is exact, and fma rounds the exact u*s - 128 s once).
+    uint32_t e0 = d0 ^ 0x80808080u, e1 = d1 ^ 0x80808080u;
+    float f0 = (float)(e0 & 0xFF), f1 = (float)((e0 >> 8) & 0xFF);
+    float f2 = (float)((e0 >> 16) & 0xFF), f3 = (float)(e0 >> 24);
+    float f4 = (float)(e1 & 0xFF), f5 = (float)((e1 >> 8) & 0xFF);
+    float f6 = (float)((e1 >> 16) & 0xFF), f7 = (float)(e1 >> 24);
+    r.x = pack_bf16x2(__builtin_fmaf(f0, s, s_m128), __builtin_fmaf(f1, s, s_m128));
+    r.y = pack_bf16x2(__builtin_fmaf(f2, s, s_m128), __builtin_fmaf(f3, s, s_m128));
+    r.z = pack_bf16x2(__builtin_fmaf(f4, s, s_m128), __builtin_fmaf(f5, s, s_m128));
+    r.w = pack_bf16x2(__builtin_fmaf(f6, s, s_m128), __builtin_fmaf(f7, s, s_m128));
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+// 16x16 output tiles; lane l holds D[4*(l/16) + j][l % 16], j = 0..3.
+// A operand: row l % 16, B operand: column l % 16; both carry the same k slots,
+// so any assignment of real k indices to slots that A and B share is valid.
+
+__device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4 mfma_i8_k64(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// fp8 (e4m3) x fp8 (e4m3), K = 128: format selectors 0/0, no block scaling.
+__device__ __forceinline__ f32x4 mfma_fp8_k128(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
+  i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- memory helpers
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Workgroup -> logical index remap so that consecutive logical indices land on
+// the same XCD (dispatch sends workgroup b to XCD b % 8).  Bijective on [0, T).
+__device__ __forceinline__ int xcd_remap(int b, int T) {
+  constexpr int kXcd = 8;
+  int q = T / kXcd, r = T % kXcd;
+  int x = b % kXcd, li = b / kXcd;
+  int start = x * q + (x < r ? x : r);
+  return start + li;
+}
+
+}  // namespace qlq

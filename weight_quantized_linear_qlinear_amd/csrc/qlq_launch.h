@@ -1,0 +1,54 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlq {
+
+enum Scheme : int { kW8A16 = 0, kW8A8 = 1 };
+
+// How one GEMM call is cut into workgroups.
+struct GemmPlan {
+  int kind = 0;             // 0: small-M family (M <= 16), 1: large-M MFMA family
+  int S = 1;                // split-K factor (workgroups sharing one output tile)
+  int units_per_split = 0;  // K units (64 or 128 inputs) per split
+  int units_per_wave = 0;   // small-M: K units per wave
+  int BM = 0, BN = 0;       // large-M: workgroup tile
+  int tiles = 0;            // output tiles (small: 16-column blocks)
+  int grid = 0;             // workgroups launched
+  size_t ws_bytes = 0;      // workspace: counters + split-K partials
+  size_t ws_counter_bytes = 0;
+};
+
+GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N);
+
+// Arguments every GEMM kernel receives (plain pointers and sizes).
+struct GemmArgs {
+  const void* x;            // bf16 [M,K] (W8A16) or 1-byte codes [M,K] (W8A8)
+  const uint8_t* w;         // packed weight tiles
+  const float* w_scale;     // [N] or [1]
+  int scale_per_tensor;
+  void* y;                  // bf16 [M,N], or int32/fp32 [M,N] accumulators
+  uint32_t* counters;       // [tiles] arrival counters (split-K only)
+  float* partials;          // split-K partial sums
+  int M, K, N, KT, NT;
+  float input_scale;
+  int out_acc;
+  int fast;                 // K % 64 == 0 and 16-byte aligned rows/pointers
+};
+
+hipError_t launch_gemm_small(int scheme, int qtype, const GemmPlan& plan, const GemmArgs& a,
+                             hipStream_t st);
+hipError_t launch_gemm_large(int scheme, int qtype, const GemmPlan& plan, const GemmArgs& a,
+                             hipStream_t st);
+
+hipError_t launch_absmax_scale(const void* src, int is_bf16, int64_t numel, float qmax, float* out,
+                               hipStream_t st);
+hipError_t launch_pack_weight(const void* w, int is_bf16, int N, int K, int qtype, int per_tensor,
+                              uint8_t* packed, float* w_scale, hipStream_t st);
+hipError_t launch_unpack_weight(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st);
+hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st);
+
+}  // namespace qlq
