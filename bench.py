@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized linear layer on one MI355X: the 3B-scale linear stack.
+
+Workload (the pages' "3B-scale config": hidden 2048, intermediate 11008, 36
+layers; their linear-backend microbench runs q_proj / up_proj / down_proj at
+M = 1, 16, 256, 1024 tokens -- "Nano-vLLM-MoE" README, section "FP8 W8A8 static
+quantization"):
+  36 layers x {q_proj 2048->2048, up_proj 2048->11008, down_proj 11008->2048},
+  chained (each output is the next input), in two variants
+    * INT8 W8A16 (per-channel weight scales), and
+    * FP8 W8A8 static (per-tensor weight scale, per-layer input scales
+      calibrated offline on a 64-row batch through the bf16-dequant chain),
+  swept over M in {1, 16, 256, 1024}.
+One step = the 8 chains (2 variants x 4 M) = 864 GEMMs (+ 432 activation
+quantizations).  Each chain is captured once as a HIP graph and replayed, so
+the timed region holds GPU work only; weights (1.65 GiB per variant) are far
+larger than the 256 MB last-level cache, so every step streams them from HBM.
+
+Output: one JSON line on stdout.  `value` is the whole step's TFLOP/s (2 M N K
+per GEMM); `cases` gives us, TFLOP/s, algorithmic GB/s and roofline fractions per
+(variant, M); `roofline` is for the dominant kernel; `cpu_baseline` times the
+oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qlinear µs, TFLOP/s and HBM GB/s at M=1/16/256/1024; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
+VARIANTS = (("int8_w8a16", "w8a16", "int8", "per_channel"),
+            ("fp8_w8a8_static", "w8a8_static", "fp8_e4m3fn", "per_tensor"))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_bytes(scheme, M, K, N, per_tensor):
+    """Algorithmic HBM bytes of one GEMM call (codes + scales + activations in + out)."""
+    scale = 4 if per_tensor else 4 * N
+    if scheme == "w8a16":
+        return N * K + scale + 2 * M * K + 2 * M * N
+    return N * K + scale + M * K + 2 * M * N
+
+
+def act_quant_bytes(M, K):
+    return 2 * M * K + M * K
+
+
+def build_stack(qlq, synth, torch, dev, seed, layers):
+    """Quantized weights of both variants and the calibrated FP8 input scales."""
+    import numpy as np
+    qi, qf = [], []
+    t0 = time.time()
+    for l in range(layers):
+        ri, rf = [], []
+        for p in range(3):
+            w = synth.stack_weight(seed, l, p, dev)
+            ri.append(qlq.quantize_weight(w, "int8", "per_channel"))
+            rf.append(qlq.quantize_weight(w, "fp8_e4m3fn", "per_tensor"))
+            del w
+        qi.append(ri)
+        qf.append(rf)
+    torch.cuda.synchronize()
+    log(f"[bench] quantized {layers}x3 weights in {time.time() - t0:.1f}s")
+    # offline calibration: a 64-row batch through the bf16-dequant chain of the FP8 weights
+    calib, _ = synth.stack_inputs(seed, 1)
+    h = torch.from_numpy(np.ascontiguousarray(calib).view(np.int16)).view(torch.bfloat16).to(dev)
+    scales = torch.empty(layers * 3, dtype=torch.float32, device=dev)
+    for l in range(layers):
+        for p in range(3):
+            qlq.calibrate_input_scale(h, "fp8_e4m3fn", out=scales[3 * l + p: 3 * l + p + 1])
+            h = qlq.qlinear_w8a16(h, qf[l][p])
+    sx = scales.cpu().tolist()
+    return qi, qf, [[sx[3 * l + p] for p in range(3)] for l in range(layers)]
+
+
+def cpu_baseline(seed, layers_w, sx):
+    """Time the oracle on layer 0 of the stack (both variants, every M)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
+    except Exception:
+        threads = os.cpu_count()
+    # offline steps (not timed): the oracle's own quantized weights
+    w_host = [w.cpu().numpy() for w in layers_w]
+    qi = [oracle.quantize_weight(w, "int8", "per_channel") for w in w_host]
+    qf = [oracle.quantize_weight(w, "fp8_e4m3fn", "per_tensor") for w in w_host]
+    flops = 0
+    t0 = time.perf_counter()
+    for M in synth.STACK_M:
+        _, x = synth.stack_inputs(seed, M)
+        h = x
+        for p, (_, K, N) in enumerate(synth.STACK_PROJS):
+            h = oracle.qlinear_w8a16(h, qi[p][0], qi[p][1], "int8")
+            flops += 2 * M * N * K
+        h = x
+        for p, (_, K, N) in enumerate(synth.STACK_PROJS):
+            s = np.float32(sx[p])
+            xq = oracle.quantize_act_static(h, s, "fp8_e4m3fn")
+            h = oracle.qlinear_w8a8_static(xq, s, qf[p][0], qf[p][1], "fp8_e4m3fn")
+            flops += 2 * M * N * K
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt, "cpu": platform.processor() or platform.machine(),
+            "sample": "layer 0 of the stack (q_proj, up_proj, down_proj chained), INT8 W8A16 and FP8 W8A8 "
+                      "(activation quantization included, offline weight quantization and calibration "
+                      "excluded), M in {1,16,256,1024}; float64 NumPy oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=36, help="decoder layers in the stack (36 = the pages' config)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the quantized linear layer runs on a single MI355X here "
+              "(multi-GPU sharding is described in DESIGN.md, not run). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import weight_quantized_linear_qlinear_amd as qlq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = args.layers
+    qi, qf, sx = build_stack(qlq, synth, torch, dev, args.seed, L)
+    variants = {"int8_w8a16": qi, "fp8_w8a8_static": qf}
+
+    # buffers: inputs per M, ping-pong activations, codes, one shared workspace
+    Ms = synth.STACK_M
+    Mmax = max(Ms)
+    x0 = {}
+    for M in Ms:
+        _, x = synth.stack_inputs(args.seed, M)
+        x0[M] = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    hbuf = [torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    xqbuf = torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.uint8, device=dev)
+    ws_need = 0
+    for _, scheme, qtype, _ in VARIANTS:
+        for M in Ms:
+            for _, K, N in synth.STACK_PROJS:
+                ws_need = max(ws_need, qlq.workspace_bytes(scheme, M, K, N, qtype))
+    ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
+
+    def chain(vname, M):
+        scheme = "w8a16" if vname == "int8_w8a16" else "w8a8_static"
+        h = x0[M]
+        i = 0
+        for l in range(L):
+            for p, (_, K, N) in enumerate(synth.STACK_PROJS):
+                out = hbuf[i % 2][: M * N].view(M, N)
+                qw = variants[vname][l][p]
+                if scheme == "w8a16":
+                    qlq.qlinear_w8a16(h, qw, out=out, workspace=ws)
+                else:
+                    xq = qlq.quantize_act_static(h, sx[l][p], "fp8_e4m3fn", out=xqbuf[: M * K].view(M, K))
+                    qlq.qlinear_w8a8_static(xq, sx[l][p], qw, out=out, workspace=ws)
+                h = out
+                i += 1
+        return h
+
+    # capture one graph per (variant, M)
+    cases = [(v[0], M) for v in VARIANTS for M in Ms]
+    graphs = {}
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for c in cases:
+        chain(*c)                                   # eager warm-up outside capture
+    torch.cuda.synchronize()
+    for c in cases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            chain(*c)
+        graphs[c] = g
+    torch.cuda.synchronize()
+    log(f"[bench] captured {len(graphs)} graphs of {3 * L} GEMMs each")
+
+    cur = torch.cuda.current_stream()
+    ev = {c: [] for c in cases}
+
+    def step(timed):
+        for c in cases:
+            if timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(cur)
+                graphs[c].replay()
+                e1.record(cur)
+                ev[c].append((e0, e1))
+            else:
+                graphs[c].replay()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-case figures
+    out_cases = {}
+    tot_flops = 0
+    groups = {}
+    for vname, scheme, qtype, gran in VARIANTS:
+        for M in Ms:
+            us = sum(a.elapsed_time(b) for a, b in ev[(vname, M)]) * 1e3 / args.steps
+            flops = sum(2 * M * N * K for _, K, N in synth.STACK_PROJS) * L
+            byts = sum(gemm_bytes(scheme, M, K, N, gran == "per_tensor") +
+                       (act_quant_bytes(M, K) if scheme == "w8a8_static" else 0)
+                       for _, K, N in synth.STACK_PROJS) * L
+            dt = "bf16" if scheme == "w8a16" else "fp8"
+            t_hbm = byts / (HBM_PEAK_GBS * 1e9) * 1e6
+            t_mfma = flops / (MFMA_PEAK_TFLOPS[dt] * 1e12) * 1e6
+            tot_flops += flops
+            out_cases[f"{vname}/M={M}"] = {
+                "us_per_stack": round(us, 2), "us_per_gemm": round(us / (3 * L), 3),
+                "tflops": round(flops / us / 1e6, 2), "gbs": round(byts / us / 1e3, 1),
+                "hbm_frac": round(t_hbm / us, 3), "mfma_frac": round(t_mfma / us, 3),
+                "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                "frac": round(max(t_hbm, t_mfma) / us, 3)}
+            fam = (vname, "small" if M <= 16 else "large")
+            g = groups.setdefault(fam, {"us": 0.0, "flops": 0, "bytes": 0, "launches": 0, "dt": dt})
+            g["us"] += us
+            g["flops"] += flops
+            g["bytes"] += byts
+            g["launches"] += 3 * L
+    # dominant kernel: the (variant, kernel family) group with the most time
+    fam, g = max(groups.items(), key=lambda kv: kv[1]["us"])
+    avg_us = g["us"] / g["launches"]
+    t_hbm = g["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6
+    t_mfma = g["flops"] / (MFMA_PEAK_TFLOPS[g["dt"]] * 1e12) * 1e6
+    if t_mfma >= t_hbm:
+        achieved = g["flops"] / g["launches"] / (avg_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[g["dt"]],
+                "unit": "TFLOP/s"}
+    else:
+        achieved = g["bytes"] / g["launches"] / (avg_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 3)
+    roof["traffic"] = None
+    kernel_name = {("int8_w8a16", "large"): "gemm_large_kernel<int8, W8A16>",
+                   ("int8_w8a16", "small"): "gemm_small_kernel<int8, W8A16>",
+                   ("fp8_w8a8_static", "large"): "gemm_large_kernel<fp8, W8A8> + quant_act_kernel<fp8>",
+                   ("fp8_w8a8_static", "small"): "gemm_small_kernel<fp8, W8A8> + quant_act_kernel<fp8>"}[fam]
+    roof["kernel"] = kernel_name
+    roof["avg_launch_us"] = round(avg_us, 3)
+    roof["launches_per_step"] = g["launches"]
+
+    value = tot_flops / (ms_per_step * 1e-3) / 1e12
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp8", "data": "synthetic",
+            "config": {"workload": f"3B-scale linear stack: {L} layers x {{q_proj 2048->2048, up_proj "
+                                   f"2048->11008, down_proj 11008->2048}} chained; INT8 W8A16 and FP8 W8A8 "
+                                   f"static; M in {{1,16,256,1024}}; one HIP graph per chain",
+                       "layers": L, "M": list(Ms), "variants": [v[0] for v in VARIANTS],
+                       "gemms_per_step": 3 * L * len(cases)},
+            "cases": out_cases, "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on its sample ...")
+        layer0 = [synth.stack_weight(args.seed, 0, p, dev) for p in range(3)]
+        line["cpu_baseline"] = cpu_baseline(args.seed, layer0, sx[0])
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,10 +18,12 @@ down_proj of that model at four token counts -- "Nano-vLLM-MoE" README, section
   bf16 with round-to-nearest-even (torch's CPU cast, an independent library);
 * draw order inside one single-GEMM case: W, then the 64-row calibration
   batch, then x;
-* the 36-layer stack draws each (layer, projection) weight from its own
-  stream ``default_rng((seed, layer, proj))`` so any layer can be produced
-  without drawing the ones before it; its calibration batch and input come
-  from ``default_rng((seed, 1000))`` in that order.
+* the 36-layer stack (1.76 G weights) draws each (layer, projection) weight on
+  the device with torch's Philox generator seeded with
+  ``seed * 1000003 + 3 * layer + proj + 1`` (``torch.randn`` in fp32, times
+  0.02), so any layer can be produced without drawing the ones before it and
+  without minutes of host RNG; its calibration batch and input come from
+  ``default_rng((seed, 1000))`` in that order.
 """
 from __future__ import annotations
 
@@ -114,10 +116,16 @@ def small_inputs(seed: int, M: int, K: int, N: int, w_std: float = WEIGHT_STD):
     return w, calib, x
 
 
-def stack_weight(seed: int, layer: int, proj: int) -> np.ndarray:
-    """Weight of projection ``proj`` (0 q, 1 up, 2 down) of decoder layer ``layer``."""
+def stack_weight(seed: int, layer: int, proj: int, device) -> torch.Tensor:
+    """fp32 weight of projection ``proj`` (0 q, 1 up, 2 down) of decoder layer ``layer``.
+
+    Drawn on ``device`` (the recipe is defined for a GPU device; a CPU device
+    gives a different, equally seeded stream).
+    """
     _, K, N = STACK_PROJS[proj]
-    return weight(np.random.default_rng((seed, layer, proj)), N, K)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + 3 * layer + proj + 1)
+    return torch.randn((N, K), generator=g, device=device, dtype=torch.float32).mul_(WEIGHT_STD)
 
 
 def stack_inputs(seed: int, M: int):

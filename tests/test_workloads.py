@@ -2,6 +2,7 @@
 import os
 
 import numpy as np
+import torch
 
 import synth
 
@@ -42,6 +43,10 @@ def test_inputs_are_seeded_and_shaped():
     assert a.x.shape == (1, 2048) and a.x.dtype == np.uint16
     assert a.calib.shape == (64, 2048)
     assert abs(float(a.w.std()) - 0.02) < 1e-3
-    w0 = synth.stack_weight(0, 3, 1)
-    assert w0.shape == (11008, 2048) and np.array_equal(w0, synth.stack_weight(0, 3, 1))
-    assert not np.array_equal(w0[:2048, :], synth.stack_weight(0, 3, 0)[:, :])
+    w0 = synth.stack_weight(0, 3, 1, "cpu")
+    assert w0.shape == (11008, 2048) and w0.dtype == torch.float32
+    assert torch.equal(w0, synth.stack_weight(0, 3, 1, "cpu"))
+    assert not torch.equal(w0[:2048, :], synth.stack_weight(0, 3, 0, "cpu"))
+    assert abs(float(w0.std()) - 0.02) < 1e-3
+    calib, x = synth.stack_inputs(0, 16)
+    assert calib.shape == (64, 2048) and x.shape == (16, 2048)
