@@ -202,3 +202,20 @@ def test_split_k_plans_interleaved_on_one_workspace():
                     assert np.array_equal(acc, ref)
                 else:
                     check_close(acc, ref)
+
+
+@pytest.mark.parametrize("MKN", [(1, 11008, 2048), (256, 11008, 2048), (16, 2048, 2048)])
+def test_split_k_int8_repeated_bit_exact(MKN):
+    # Split-K slices may land on different XCDs; the integer accumulators must
+    # come out identical to the oracle on every one of many repeated calls.
+    M, K, N = MKN
+    assert qlq.workspace_bytes("w8a8_static", M, K, N, "int8") > 0
+    _, calib, x, qw, q_ref, s_ref = _prep(901 + M, M, K, N, "int8")
+    sx = oracle.calibrate_input_scale(calib, "int8")
+    ref = oracle.qlinear_w8a8_static(oracle.quantize_act_static(x, sx, "int8"), sx, q_ref, s_ref, "int8", out="acc")
+    xq = qlq.quantize_act_static(bf16_to_gpu(x), float(sx), "int8")
+    out = torch.empty((M, N), dtype=torch.int32, device=dev())
+    for rep in range(20):
+        out.fill_(-1)
+        qlq.qlinear_w8a8_static(xq, float(sx), qw, "acc", out=out)
+        assert np.array_equal(out.cpu().numpy(), ref), f"rep {rep}"

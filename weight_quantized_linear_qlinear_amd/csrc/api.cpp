@@ -40,6 +40,7 @@ constexpr int64_t kMaxInt8K = 133144;                // 127 * 127 * K < 2^31
 // plan, so partial sums of one call never land on counters of another.
 constexpr int64_t kMaxSplitTiles = 1024;
 constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
+constexpr int64_t kSmallUnitsPerWave = 8;   // matches kUnroll of the small-M kernel
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -76,12 +77,16 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N) {
     p.kind = 0;
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
     const int64_t KU = cdiv(KT, TPU);
-    int64_t S = 1;
+    // Each wave handles at most kSmallUnitsPerWave K units (all its loads go out
+    // before the first wait); small column counts are also split to fill the GPU.
+    int64_t S = cdiv(KU, 4 * kSmallUnitsPerWave);
     if (NT < 512) {   // NT < 512 <= kMaxSplitTiles
-      S = cdiv(512, NT);
+      int64_t want = cdiv(512, NT);
       int64_t cap = KU / 4 > 1 ? KU / 4 : 1;
-      if (S > cap) S = cap;
+      if (want > cap) want = cap;
+      if (want > S) S = want;
     }
+    if (S > 1 && NT > kMaxSplitTiles) S = 1;   // cannot happen for K < 2^24 with the bound above
     const int64_t ups = cdiv(KU, S);
     S = cdiv(KU, ups);
     p.S = (int)S;

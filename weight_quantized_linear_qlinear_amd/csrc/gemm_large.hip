@@ -249,16 +249,16 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        part[(i * TN + j) * 256 + tid] = T::kIntAcc ? __builtin_bit_cast(f32x4, acci[i][j]) : accf[i][j];
-    __threadfence();
-    __syncthreads();
+        store_partial(&part[(i * TN + j) * 256 + tid],
+                      T::kIntAcc ? __builtin_bit_cast(f32x4, acci[i][j]) : accf[i][j]);
+    wait_stores_performed();
     __shared__ uint32_t s_prev;
-    if (tid == 0) s_prev = atomicAdd(&a.counters[tile_id], 1u);
+    __syncthreads();
+    if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
     __syncthreads();
     if (s_prev != (uint32_t)(S - 1)) return;
-    __threadfence();
     const int64_t slice = (int64_t)tiles_m * tiles_n * NV * 256;
-    f32x4* base = reinterpret_cast<f32x4*>(a.partials) + (int64_t)tile_id * NV * 256;
+    const f32x4* base = reinterpret_cast<const f32x4*>(a.partials) + (int64_t)tile_id * NV * 256;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -267,15 +267,15 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
         if constexpr (T::kIntAcc) {
           i32x4 t = {0, 0, 0, 0};
           for (int q = 0; q < S; ++q)
-            t += q == s ? acci[i][j] : __builtin_bit_cast(i32x4, __builtin_nontemporal_load(base + q * slice + v));
+            t += q == s ? acci[i][j] : __builtin_bit_cast(i32x4, load_partial(base + q * slice + v));
           acci[i][j] = t;
         } else {
           f32x4 t = {0.f, 0.f, 0.f, 0.f};
-          for (int q = 0; q < S; ++q) t += q == s ? accf[i][j] : __builtin_nontemporal_load(base + q * slice + v);
+          for (int q = 0; q < S; ++q) t += q == s ? accf[i][j] : load_partial(base + q * slice + v);
           accf[i][j] = t;
         }
       }
-    if (tid == 0) a.counters[tile_id] = 0u;
+    if (tid == 0) reset_counter(&a.counters[tile_id]);
   }
 
   // ---- epilogue: block (i, j), lane (r, g), value jj -> y[m, n]

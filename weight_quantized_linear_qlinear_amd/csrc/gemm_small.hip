@@ -15,7 +15,8 @@
 // s-th slice of K; its four waves take consecutive sub-slices.  The four wave
 // accumulators are summed through LDS; with S > 1 slices per column block the
 // partial sums go to the workspace and the last workgroup to arrive adds them
-// in slice order (deterministic) and runs the epilogue.
+// in slice order (deterministic) and runs the epilogue.  The handoff uses
+// agent-coherent partial stores and a device atomic counter (qlq_device.h).
 #include "qlq_device.h"
 #include "qlq_launch.h"
 
@@ -95,43 +96,45 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
   f32x4 accf = {0.f, 0.f, 0.f, 0.f};
   i32x4 acci = {0, 0, 0, 0};
 
+  // All loads of the wave's K slice (at most kUnroll units, see plan_gemm) are
+  // issued before the first wait: one memory round trip per wave.
   for (int u0 = u_begin; u0 < u_end; u0 += kUnroll) {
     u32x4 wv[kUnroll][TPU];
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i)
-#pragma unroll
-      for (int t = 0; t < TPU; ++t) {
-        int kt = (u0 + i) * TPU + t;
-        wv[i][t] = (u0 + i < u_end && kt < a.KT) ? ld16_stream(wbase + (int64_t)kt * kTileBytes)
-                                                  : (u32x4){0u, 0u, 0u, 0u};
-      }
+    u32x4 xa[kUnroll][TPU];      // A operand bytes: 16 codes, or 8 bf16 (W8A16 uses 2 regs per unit)
+    u32x4 xb[kUnroll];           // W8A16: bf16 k + 8 .. k + 15
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int u = u0 + i;
-      if (u >= u_end) break;
+      const bool live = u0 + i < u_end;
+#pragma unroll
+      for (int t = 0; t < TPU; ++t) {
+        const int kt = (u0 + i) * TPU + t;
+        const bool ok = live && kt < a.KT;
+        wv[i][t] = ok ? ld16_stream(wbase + (int64_t)kt * kTileBytes) : (u32x4){0u, 0u, 0u, 0u};
+        xa[i][t] = (u32x4){0u, 0u, 0u, 0u};
+        if constexpr (SCH == kW8A16) {
+          xb[i] = (u32x4){0u, 0u, 0u, 0u};
+          if (ok && row_ok)
+            load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, kt * kTileK + g * 16,
+                                 a.K, xa[i][t], xb[i]);
+        } else {
+          if (ok && row_ok)
+            xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K,
+                                            kt * kTileK + g * 16, a.K);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      if (u0 + i >= u_end) break;
       if constexpr (SCH == kW8A16) {
-        u32x4 xlo = {0u, 0u, 0u, 0u}, xhi = {0u, 0u, 0u, 0u};
-        if (row_ok)
-          load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, u * kTileK + g * 16,
-                               a.K, xlo, xhi);
         bf16x8 b0 = dequant8<QT>(wv[i][0].x, wv[i][0].y, sc, sc_m128);
         bf16x8 b1 = dequant8<QT>(wv[i][0].z, wv[i][0].w, sc, sc_m128);
-        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xlo), b0, accf);
-        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xhi), b1, accf);
+        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[i][0]), b0, accf);
+        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[i]), b1, accf);
+      } else if constexpr (QT == kInt8) {
+        acci = mfma_i8_k64(xa[i][0], wv[i][0], acci);
       } else {
-        const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K;
-        if constexpr (QT == kInt8) {
-          u32x4 xa = {0u, 0u, 0u, 0u};
-          if (row_ok) xa = load_x_codes16<FAST>(xrow, u * kTileK + g * 16, a.K);
-          acci = mfma_i8_k64(xa, wv[i][0], acci);
-        } else {
-          u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-          if (row_ok) {
-            x0 = load_x_codes16<FAST>(xrow, (2 * u) * kTileK + g * 16, a.K);
-            if (2 * u + 1 < a.KT) x1 = load_x_codes16<FAST>(xrow, (2 * u + 1) * kTileK + g * 16, a.K);
-          }
-          accf = mfma_fp8_k128(x0, x1, wv[i][0], wv[i][1], accf);
-        }
+        accf = mfma_fp8_k128(xa[i][0], xa[i][TPU - 1], wv[i][0], wv[i][TPU - 1], accf);
       }
     }
   }
@@ -155,26 +158,25 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
   // ---- split-K: publish, count arrivals, last one sums the slices in order
   if (S > 1) {
     f32x4* part = reinterpret_cast<f32x4*>(a.partials);
-    part[((int64_t)s * a.NT + nt) * 64 + lane] = tot;
-    __threadfence();
+    store_partial(&part[((int64_t)s * a.NT + nt) * 64 + lane], tot);
+    wait_stores_performed();
     uint32_t prev = 0;
-    if (lane == 0) prev = atomicAdd(&a.counters[nt], 1u);
+    if (lane == 0) prev = arrive(&a.counters[nt]);
     prev = __shfl(prev, 0, 64);
     if (prev != (uint32_t)(S - 1)) return;
-    __threadfence();
     if constexpr (T::kIntAcc) {
       i32x4 t = {0, 0, 0, 0};
       for (int q = 0; q < S; ++q)
         t += (q == s) ? __builtin_bit_cast(i32x4, tot)
-                      : __builtin_bit_cast(i32x4, __builtin_nontemporal_load(&part[((int64_t)q * a.NT + nt) * 64 + lane]));
+                      : __builtin_bit_cast(i32x4, load_partial(&part[((int64_t)q * a.NT + nt) * 64 + lane]));
       tot = __builtin_bit_cast(f32x4, t);
     } else {
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
       for (int q = 0; q < S; ++q)
-        t += (q == s) ? tot : __builtin_nontemporal_load(&part[((int64_t)q * a.NT + nt) * 64 + lane]);
+        t += (q == s) ? tot : load_partial(&part[((int64_t)q * a.NT + nt) * 64 + lane]);
       tot = t;
     }
-    if (lane == 0) a.counters[nt] = 0u;
+    if (lane == 0) reset_counter(&a.counters[nt]);
   }
 
   // ---- epilogue: lane holds D[4g + j][r] = y[m = 4g + j, n]

@@ -136,6 +136,40 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// ---------------------------------------------------------------- split-K handoff
+// Partial sums of one output tile, written by several workgroups, are read back
+// by the last one to arrive.  Workgroups of one launch may sit on different XCDs,
+// each with its own L2, so the partials travel through agent-coherent accesses
+// (64-bit atomic stores/loads at agent scope: the sc1 cache policy) instead of a
+// device-wide fence, which would write back and invalidate a whole L2 per
+// workgroup.  Order: partial stores -> wait until they are performed ->
+// increment the arrival counter (a device atomic).
+
+__device__ __forceinline__ void store_partial(f32x4* p, f32x4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  u32x4 b = __builtin_bit_cast(u32x4, v);
+  __hip_atomic_store(q, (uint64_t)b.x | ((uint64_t)b.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)b.z | ((uint64_t)b.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_partial(const f32x4* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x4, (u32x4){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
+}
+
+// Waits until this thread's earlier stores are performed (vmcnt = 0).
+__device__ __forceinline__ void wait_stores_performed() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup -> logical index remap so that consecutive logical indices land on
 // the same XCD (dispatch sends workgroup b to XCD b % 8).  Bijective on [0, T).
 __device__ __forceinline__ int xcd_remap(int b, int T) {
