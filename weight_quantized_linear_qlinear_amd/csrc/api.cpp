@@ -68,7 +68,59 @@ qlq_status check_scale(float s, const char* name) {
 
 namespace qlq {
 
-GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N) {
+namespace {
+
+// Direct-to-LDS MFMA kernel: choose the tile configuration and split-K factor
+// that minimise the estimated makespan on 256 CUs.  Per-configuration figures
+// were measured on MI355X (time of one 64-input stage of one workgroup, and
+// workgroups resident per CU):
+//   cfg 0 (256 x 256): W8A16 2.84 us, W8A8 1.08 us, 1 per CU
+//   cfg 1 (128 x 256): W8A16 1.50 us, W8A8 0.90 us, 1 per CU
+//   cfg 2 (128 x 128): W8A16 1.08 us (1 per CU), W8A8 0.68 us (2 per CU)
+// Split-K adds its fp32/int32 partial traffic (written and read once each).
+GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
+  constexpr int64_t kCUs = 256;
+  const int64_t KT = cdiv(K, 64);
+  const double stage_us[2][3] = {{2.84, 1.50, 1.08}, {1.08, 0.90, 0.68}};
+  const int per_cu[2][3] = {{1, 1, 1}, {1, 1, 2}};
+  const int sch = scheme == kW8A16 ? 0 : 1;
+  GemmPlan best;
+  double best_cost = 1e300;
+  for (int cfg = 0; cfg < 3; ++cfg) {
+    const int64_t BM = mfma_cfg_tile_m(cfg), BN = mfma_cfg_tile_n(cfg);
+    const int64_t tiles = cdiv(M, BM) * cdiv(N, BN);
+    for (int64_t S = 1; S <= 16; ++S) {
+      if (S > 1 && (tiles > kMaxSplitTiles || KT / S < 2)) break;
+      const int64_t ups = cdiv(KT, S);
+      if (cdiv(KT, ups) != S) continue;
+      const int64_t rounds = cdiv(tiles * S, kCUs * per_cu[sch][cfg]);
+      double cost = (double)rounds * ((double)ups * stage_us[sch][cfg] + 1.0);
+      if (S > 1) cost += (double)(S * tiles * BM * BN * 4 * 2) / 5.0e6 + 1.0;   // bytes / (5 TB/s), in us
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = GemmPlan();
+        best.kind = 2;
+        best.cfg = cfg;
+        best.BM = (int)BM;
+        best.BN = (int)BN;
+        best.S = (int)S;
+        best.units_per_split = (int)ups;
+        best.tiles = (int)tiles;
+        best.grid = (int)(tiles * S);
+        if (S > 1) {   // one fp32/int32 partial per output element and slice
+          best.ws_counter_bytes = kCounterBytes;
+          best.ws_bytes = kCounterBytes + (size_t)S * tiles * BM * BN * 4;
+        }
+      }
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool fast) {
+  if (M > 16 && fast && K % 64 == 0) return plan_mfma(scheme, M, K, N);
   GemmPlan p;
   const int64_t KT = cdiv(K, 64), NT = cdiv(N, 16);
   if (M <= 16) {
@@ -152,7 +204,10 @@ size_t qlq_packed_weight_bytes(int64_t N, int64_t K) {
 size_t qlq_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype) {
   if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
   if (scheme != QLQ_SCHEME_W8A16 && scheme != QLQ_SCHEME_W8A8_STATIC) return 0;
-  return qlq::plan_gemm((int)scheme, (int)qtype, M, K, N).ws_bytes;
+  // The call picks the direct-to-LDS kernel only for aligned x; size for both.
+  const size_t a = qlq::plan_gemm((int)scheme, (int)qtype, M, K, N, true).ws_bytes;
+  const size_t b = qlq::plan_gemm((int)scheme, (int)qtype, M, K, N, false).ws_bytes;
+  return a > b ? a : b;
 }
 
 qlq_status qlq_quantize_weight(const void* w, int w_is_bf16, int64_t N, int64_t K, qlq_qtype qtype,
@@ -213,8 +268,11 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   if (!aligned(wq_packed, 16)) return fail(QLQ_ERR_INVALID_ARG, "wq_packed must be 16-byte aligned");
   if (!aligned(w_scale, 4) || !aligned(y, 4) || !aligned(x, scheme == qlq::kW8A16 ? 2 : 1))
     return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
-  qlq::GemmPlan plan = qlq::plan_gemm(scheme, (int)qtype, M, K, N);
+  const bool fast = (K % 64 == 0) && aligned(x, 16);
+  qlq::GemmPlan plan = qlq::plan_gemm(scheme, (int)qtype, M, K, N, fast);
   if (plan.ws_bytes > 0) {
+    if (plan.ws_bytes - plan.ws_counter_bytes >= ((size_t)1 << 31))
+      return fail(QLQ_ERR_UNSUPPORTED, "split-K partials above 2 GiB");
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(QLQ_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", plan.ws_bytes,
                   workspace ? workspace_bytes : (size_t)0);
@@ -229,6 +287,7 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.counters = plan.ws_bytes ? static_cast<uint32_t*>(workspace) : nullptr;
   a.partials = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_counter_bytes)
                              : nullptr;
+  a.partials_bytes = plan.ws_bytes ? (uint32_t)(plan.ws_bytes - plan.ws_counter_bytes) : 0u;
   a.M = (int)M;
   a.K = (int)K;
   a.N = (int)N;
@@ -236,9 +295,10 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.NT = (int)cdiv(N, 16);
   a.input_scale = input_scale;
   a.out_acc = out_acc;
-  a.fast = (K % 64 == 0) && aligned(x, 16);
-  hipError_t e = plan.kind == 0 ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
-                                : qlq::launch_gemm_large(scheme, (int)qtype, plan, a, stream);
+  a.fast = fast;
+  hipError_t e = plan.kind == 0   ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
+                 : plan.kind == 1 ? qlq::launch_gemm_large(scheme, (int)qtype, plan, a, stream)
+                                  : qlq::launch_gemm_mfma(scheme, (int)qtype, plan, a, stream);
   return hip_status(e, scheme == qlq::kW8A16 ? "qlinear_w8a16" : "qlinear_w8a8_static");
 }
 

@@ -244,12 +244,13 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
   // ---- split-K: publish partials in register order, last arrival sums in order
   constexpr int NV = TM * TN;   // f32x4 values per thread
   if (S > 1) {
-    f32x4* part = reinterpret_cast<f32x4*>(a.partials) + ((int64_t)s * tiles_m * tiles_n + tile_id) * NV * 256;
+    const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
+    const int64_t mine = ((int64_t)s * tiles_m * tiles_n + tile_id) * NV * 256;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        store_partial(&part[(i * TN + j) * 256 + tid],
+        store_partial(part, mine + (i * TN + j) * 256 + tid,
                       T::kIntAcc ? __builtin_bit_cast(f32x4, acci[i][j]) : accf[i][j]);
     wait_stores_performed();
     __shared__ uint32_t s_prev;
@@ -257,24 +258,26 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
     if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
     __syncthreads();
     if (s_prev != (uint32_t)(S - 1)) return;
+    // slices summed in order 0..S-1 (deterministic), each slice loaded at once
     const int64_t slice = (int64_t)tiles_m * tiles_n * NV * 256;
-    const f32x4* base = reinterpret_cast<const f32x4*>(a.partials) + (int64_t)tile_id * NV * 256;
+    const int64_t base = (int64_t)tile_id * NV * 256;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int v = (i * TN + j) * 256 + tid;
-        if constexpr (T::kIntAcc) {
-          i32x4 t = {0, 0, 0, 0};
-          for (int q = 0; q < S; ++q)
-            t += q == s ? acci[i][j] : __builtin_bit_cast(i32x4, load_partial(base + q * slice + v));
-          acci[i][j] = t;
-        } else {
-          f32x4 t = {0.f, 0.f, 0.f, 0.f};
-          for (int q = 0; q < S; ++q) t += q == s ? accf[i][j] : load_partial(base + q * slice + v);
-          accf[i][j] = t;
-        }
+        accf[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        acci[i][j] = (i32x4){0, 0, 0, 0};
       }
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const f32x4 p = load_partial(part, base + q * slice + (i * TN + j) * 256 + tid);
+          if constexpr (T::kIntAcc) acci[i][j] += __builtin_bit_cast(i32x4, p);
+          else accf[i][j] += p;
+        }
+    }
     if (tid == 0) reset_counter(&a.counters[tile_id]);
   }
 

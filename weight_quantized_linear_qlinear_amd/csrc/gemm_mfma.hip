@@ -1,0 +1,421 @@
+// Large-M (prefill) quantized GEMM on the gfx950 matrix cores, direct-to-LDS
+// pipeline.  Used when K is a multiple of 64 and x is 16-byte aligned (every
+// shape of the pages' models); other shapes take the register-staged kernel in
+// gemm_large.hip.
+//
+// Prefill is compute bound ("Nano-vLLM-MOE" mirror, Llama 3.1 8B section: prefill
+// leans on compute; "tiny-vLLM" README, "Quantization Results": prefill is the
+// weakest part of the INT8/W8A8 paths).  Design for gfx950, from measurements on
+// the part (32x32 MFMA shapes run at twice the rate of the 16x16 ones for bf16
+// and int8; LDS reads ~128 B/clk/CU; L2 -> LDS ~55 B/clk/CU):
+//  * 32x32 MFMAs: v_mfma_f32_32x32x16_bf16 (W8A16), v_mfma_i32_32x32x32_i8 and
+//    v_mfma_f32_32x32x64_f8f6f4 (W8A8);
+//  * operands move global -> LDS with global_load_lds_dwordx4 (no VGPR staging)
+//    into a ring of NSTAGE stages of 64 inputs each; the loop body is
+//    branch-free and the DMA issues, LDS reads and dequantization are
+//    interleaved between the MFMAs (sched_group_barrier);
+//  * the bf16 output tile is staged through LDS so global stores are whole
+//    16-byte chunks of rows;
+//  * A fragments land in LDS in MFMA lane order (each lane fetches its own 16
+//    bytes of x), B is the packed weight tile copied verbatim and read with
+//    per-lane addresses; every ds_read_b128 of a wave covers contiguous 128-byte
+//    groups, so there are no bank conflicts;
+//  * W8A16 dequantizes B in registers right after the LDS read:
+//    bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
+//  * large per-wave tiles (128 x 64 or 128 x 128) keep LDS traffic within budget.
+//
+// K-slot convention (A and B agree, so the sum over k is unchanged): inside a
+// 64-input stage, chunk c covers inputs 16c .. 16c+15.  For bf16 step (p, j)
+// lane group kg (= lane / 32) holds inputs 16(2p + kg) + 8j .. +7; for int8 step
+// p it holds chunk 2p + kg; for fp8 (one MFMA per stage) it holds chunks 2kg
+// and 2kg + 1.
+#include "qlq_device.h"
+#include "qlq_launch.h"
+
+namespace qlq {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 0x3) << 14));
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+template <int QT, int SCH>
+struct MfmaTraits {
+  static constexpr int kAElem = SCH == kW8A16 ? 2 : 1;       // bytes per x element
+  // A fragments per 32-row block per stage (1 KiB each)
+  static constexpr int kAFrags = SCH == kW8A16 ? 4 : 2;
+  static constexpr bool kIntAcc = (SCH == kW8A8 && QT == kInt8);
+};
+
+template <int QT, int SCH, int BM, int BN, int WM, int WN, int NSTAGE, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, int ups, int tiles_m, int tiles_n) {
+  using T = MfmaTraits<QT, SCH>;
+  constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static_assert(WAVES_M * WAVES_N == 4, "four waves");
+  constexpr int TM = WM / 32, TN = WN / 32;                 // 32x32 blocks per wave
+  constexpr int A_FRAGS = (BM / 32) * T::kAFrags;            // per stage
+  constexpr int B_TILES = BN / 16;                           // packed tiles per stage
+  constexpr int STAGE = (A_FRAGS + B_TILES) * 1024;
+  constexpr int A_PER_WAVE = A_FRAGS / 4, B_PER_WAVE = B_TILES / 4;
+  constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;             // DMA instructions per wave per stage
+  static_assert(A_FRAGS % 4 == 0 && B_TILES % 4 == 0, "DMA split");
+  static_assert(LOADS * (NSTAGE - 2) < 64, "vmcnt range");
+
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int l32 = lane & 31, kg = lane >> 5;
+
+  // tile coordinates: XCD-grouped, m fastest (tiles of one weight column block
+  // and K slice are neighbours on one XCD)
+  const int total = tiles_m * tiles_n * S;
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int tm = logical % tiles_m;
+  const int rest = logical / tiles_m;
+  const int s = rest % S;
+  const int tn = rest / S;
+  const int m0 = tm * BM, nt0 = tn * B_TILES;
+  const int tile_id = tn * tiles_m + tm;
+
+  const int st_begin = s * ups;
+  int st_end = st_begin + ups;
+  if (st_end > a.KT) st_end = a.KT;
+  const int nst = st_end - st_begin;
+
+  // ---- per-lane DMA source pointers (stage 0 of this slice); each stage adds 64 inputs
+  const uint8_t* a_src[A_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < A_PER_WAVE; ++i) {
+    const int f = wave * A_PER_WAVE + i;                     // fragment index in the stage
+    const int mb = f / T::kAFrags, q = f % T::kAFrags;
+    int row = m0 + mb * 32 + l32;
+    row = row < a.M ? row : a.M - 1;                         // rows >= M: harmless duplicate
+    int col;                                                 // element offset inside the stage
+    if constexpr (SCH == kW8A16) col = (2 * (q >> 1) + kg) * 16 + (q & 1) * 8;      // (p, j) = (q/2, q%2)
+    else if constexpr (QT == kInt8) col = (2 * q + kg) * 16;                         // step p = q
+    else col = (2 * kg + q) * 16;                                                    // half h = q
+    a_src[i] = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)row * a.K + (int64_t)st_begin * kTileK + col) * T::kAElem;
+  }
+  const uint8_t* b_src[B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < B_PER_WAVE; ++i) {
+    int ntile = nt0 + wave * B_PER_WAVE + i;
+    ntile = ntile < a.NT ? ntile : a.NT - 1;                 // columns >= N: harmless duplicate
+    b_src[i] = a.w + ((int64_t)ntile * a.KT + st_begin) * kTileBytes + lane * 16;
+  }
+
+  auto issue = [&](int st_local, int slot) {
+    uint8_t* base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_PER_WAVE; ++i)
+      dma16(a_src[i] + (int64_t)st_local * kTileK * T::kAElem, base + (wave * A_PER_WAVE + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i)
+      dma16(b_src[i] + (int64_t)st_local * kTileBytes, base + (A_FRAGS + wave * B_PER_WAVE + i) * 1024);
+  };
+
+  // ---- per-lane column scales (W8A16)
+  float sc[TN], sc_m128[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = nt0 * 16 + (wn * TN + j) * 32 + l32;
+    float v = 0.0f;
+    if (SCH == kW8A16) v = a.scale_per_tensor ? a.w_scale[0] : (n < a.N ? a.w_scale[n] : 0.0f);
+    sc[j] = v;
+    sc_m128[j] = -128.0f * v;
+  }
+
+  f32x16 accf[TM][TN];
+  i32x16 acci[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      accf[i][j] = (f32x16){};
+      acci[i][j] = (i32x16){};
+    }
+
+  // B read offset of lane (column l32 of the wave's 32-column block, chunk c)
+  auto b_off = [&](int nb32, int c) {
+    const int col = nb32 * 32 + l32;                          // column inside the workgroup tile
+    return (A_FRAGS + (col >> 4)) * 1024 + ((col & 15) + 16 * c) * 16;
+  };
+
+  auto compute = [&](const uint8_t* base) {
+    if constexpr (SCH == kW8A16) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        bf16x8 bfr[TN][2];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          u32x4 c = lds_read16(base + b_off(wn * TN + j, 2 * p + kg));
+          bfr[j][0] = dequant8<QT>(c.x, c.y, sc[j], sc_m128[j]);
+          bfr[j][1] = dequant8<QT>(c.z, c.w, sc[j], sc_m128[j]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int f = (wm * TM + i) * T::kAFrags + 2 * p + jj;
+            bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + f * 1024 + lane * 16));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j][jj], accf[i][j], 0, 0, 0);
+          }
+        }
+      }
+    } else if constexpr (QT == kInt8) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        i32x4 bfr[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[j] = __builtin_bit_cast(i32x4, lds_read16(base + b_off(wn * TN + j, 2 * p + kg)));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int f = (wm * TM + i) * T::kAFrags + p;
+          i32x4 af = __builtin_bit_cast(i32x4, lds_read16(base + f * 1024 + lane * 16));
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[j], acci[i][j], 0, 0, 0);
+        }
+      }
+    } else {
+      i32x8 bfr[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        u32x4 c0 = lds_read16(base + b_off(wn * TN + j, 2 * kg));
+        u32x4 c1 = lds_read16(base + b_off(wn * TN + j, 2 * kg + 1));
+        bfr[j] = (i32x8){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int f = (wm * TM + i) * T::kAFrags;
+        u32x4 a0 = lds_read16(base + f * 1024 + lane * 16);
+        u32x4 a1 = lds_read16(base + (f + 1) * 1024 + lane * 16);
+        i32x8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bfr[j], accf[i][j], 0, 0, 0, 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline: NSTAGE-1 stages in flight ahead of the one being consumed.
+  // The loop body is branch-free: the prefetch source is clamped to the last
+  // stage, so past the end it re-reads a valid stage into a slot nobody reads,
+  // and every iteration waits for the same vmcnt.
+  constexpr int NMFMA = (SCH == kW8A16 ? 4 : (QT == kInt8 ? 2 : 1)) * TM * TN;
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t) issue(t < nst ? t : nst - 1, t);
+  for (int t = 0; t < nst; ++t) {
+    wait_vmcnt<LOADS * (NSTAGE - 2)>();
+    __syncthreads();                                         // stage t visible; slot (t-1) free
+    const int pf = t + NSTAGE - 1 < nst ? t + NSTAGE - 1 : nst - 1;
+    issue(pf, (t + NSTAGE - 1) % NSTAGE);
+    compute(smem + (t % NSTAGE) * STAGE);
+    // interleave: spread the DMA issues and LDS reads between the MFMAs
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+      if (i < LOADS) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // VMEM (DMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      // DS read
+      if (SCH == kW8A16) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU (dequant)
+    }
+  }
+  wait_vmcnt<0>();                                           // no DMA may outlive the loop
+
+  // ---- split-K handoff (partials in register order)
+  constexpr int NV = TM * TN * 4;                            // f32x4 per thread
+  auto acc_vec = [&](int i, int j, int v) -> f32x4 {
+    if constexpr (T::kIntAcc) {
+      i32x16 c = acci[i][j];
+      return __builtin_bit_cast(f32x4, (i32x4){c[4 * v], c[4 * v + 1], c[4 * v + 2], c[4 * v + 3]});
+    } else {
+      f32x16 c = accf[i][j];
+      return (f32x4){c[4 * v], c[4 * v + 1], c[4 * v + 2], c[4 * v + 3]};
+    }
+  };
+  if constexpr (SPLIT) {
+    const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
+    const int64_t mine = ((int64_t)s * tiles_m * tiles_n + tile_id) * NV * 256;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) store_partial(part, mine + ((i * TN + j) * 4 + v) * 256 + tid, acc_vec(i, j, v));
+    wait_stores_performed();
+    __shared__ uint32_t s_prev;
+    __syncthreads();
+    if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
+    __syncthreads();
+    if (s_prev != (uint32_t)(S - 1)) return;
+    // Sum the slices in slice order 0..S-1 (independent of which workgroup
+    // arrived last, so the fp32 result is deterministic); each slice's values
+    // are loaded together, straight into the accumulator registers.
+    const int64_t slice = (int64_t)tiles_m * tiles_n * NV * 256;
+    const int64_t base = (int64_t)tile_id * NV * 256;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        accf[i][j] = (f32x16){};
+        acci[i][j] = (i32x16){};
+      }
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f32x4 p = load_partial(part, base + q * slice + ((i * TN + j) * 4 + v) * 256 + tid);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (T::kIntAcc) acci[i][j][4 * v + e] += __builtin_bit_cast(i32x4, p)[e];
+              else accf[i][j][4 * v + e] += p[e];
+            }
+          }
+    }
+    if (tid == 0) reset_counter(&a.counters[tile_id]);
+  }
+
+  // ---- epilogue.  bf16 outputs go through LDS so that global stores are whole
+  // 16-byte row chunks (a wave writes 1 KiB of contiguous rows); accumulator
+  // outputs and rows that are not 16-byte aligned are stored element by element.
+  // 32x32 block (i, j): lane holds column l32, value e at row 8 (e / 4) + 4 kg + (e % 4).
+  const bool staged = !(SCH == kW8A8 && a.out_acc) && (a.N % 8 == 0);
+  if (staged) {
+    constexpr int PITCH = BN * 2 + 16;                       // bytes per staged row (padding spreads banks)
+    constexpr int ROWS_FIT = (NSTAGE * STAGE) / PITCH;
+    constexpr int PASS_WM = (ROWS_FIT / WM) < WAVES_M ? (ROWS_FIT / WM) : WAVES_M;
+    static_assert(PASS_WM >= 1, "epilogue staging does not fit");
+    __syncthreads();                                         // every wave is done with the stage buffers
+#pragma unroll
+    for (int pass = 0; pass < WAVES_M; pass += PASS_WM) {
+      if (wm >= pass && wm < pass + PASS_WM) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = (wn * TN + j) * 32 + l32;
+          const int n = nt0 * 16 + col;
+          float comb = 1.0f;
+          if (SCH == kW8A8) comb = n < a.N ? a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]) : 0.0f;
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int row = (wm - pass) * WM + i * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
+              float v;
+              if constexpr (SCH == kW8A16) v = accf[i][j][e];
+              else v = (T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e]) * comb;
+              *reinterpret_cast<__bf16*>(smem + row * PITCH + col * 2) = (__bf16)v;
+            }
+        }
+      }
+      __syncthreads();
+      constexpr int CH = BN / 8;                             // 16-byte chunks per row
+      constexpr int ROWS = PASS_WM * WM;
+#pragma unroll 4
+      for (int c = tid; c < ROWS * CH; c += 256) {
+        const int row = c / CH, ch = c % CH;
+        const int m = m0 + pass * WM + row;
+        const int n = nt0 * 16 + ch * 8;
+        if (m < a.M && n < a.N) {
+          u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * PITCH + ch * 16);
+          __bf16* dst = reinterpret_cast<__bf16*>(a.y) + (int64_t)m * a.N + n;
+          if (n + 8 <= a.N) {
+            st16(dst, v);
+          } else {
+            const __bf16* src = reinterpret_cast<const __bf16*>(&v);
+            for (int e = 0; e < a.N - n; ++e) dst[e] = src[e];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = nt0 * 16 + (wn * TN + j) * 32 + l32;
+      if (n >= a.N) continue;
+      float comb = 0.0f;
+      if (SCH == kW8A8 && !a.out_acc) comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
+          if (m >= a.M) continue;
+          const int64_t o = (int64_t)m * a.N + n;
+          if constexpr (SCH == kW8A16) {
+            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)accf[i][j][e];
+          } else if (a.out_acc) {
+            if constexpr (T::kIntAcc) reinterpret_cast<int32_t*>(a.y)[o] = acci[i][j][e];
+            else reinterpret_cast<float*>(a.y)[o] = accf[i][j][e];
+          } else {
+            const float v = T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e];
+            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
+          }
+        }
+    }
+  }
+}
+
+template <int QT, int SCH, int BM, int BN, int WM, int WN, int NSTAGE>
+hipError_t launch_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  using T = MfmaTraits<QT, SCH>;
+  constexpr int STAGE = ((BM / 32) * T::kAFrags + BN / 16) * 1024;
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  auto k = p.S > 1 ? gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, NSTAGE, true>
+                   : gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, NSTAGE, false>;
+  static bool attr_set[2] = {false, false};     // one attribute call per instantiation
+  if (!attr_set[p.S > 1]) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
+    if (e != hipSuccess) return e;
+    attr_set[p.S > 1] = true;
+  }
+  k<<<p.grid, 256, NSTAGE * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile configurations (BM x BN workgroup tile, WM x WN per wave, LDS stages).
+// cfg 0: 256 x 256, waves 2 x 2 of 128 x 128; cfg 1: 128 x 256, waves 1 x 4 of 128 x 64;
+// cfg 2: 128 x 128, waves 2 x 2 of 64 x 64.
+hipError_t launch_gemm_mfma(int scheme, int qtype, const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+#define QLQ_CFG(QT, SCH)                                                         \
+  switch (p.cfg) {                                                               \
+    case 0: return launch_t<QT, SCH, 256, 256, 128, 128, 3>(p, a, st);           \
+    case 1: return launch_t<QT, SCH, 128, 256, 128, 64, 4>(p, a, st);            \
+    default: return launch_t<QT, SCH, 128, 128, 64, 64, 4>(p, a, st);            \
+  }
+  if (scheme == kW8A16) {
+    if (qtype == kFp8) { QLQ_CFG(kFp8, kW8A16) } else { QLQ_CFG(kInt8, kW8A16) }
+  } else {
+    if (qtype == kFp8) { QLQ_CFG(kFp8, kW8A8) } else { QLQ_CFG(kInt8, kW8A8) }
+  }
+#undef QLQ_CFG
+}
+
+int mfma_cfg_tile_m(int cfg) { return cfg == 0 ? 256 : 128; }
+int mfma_cfg_tile_n(int cfg) { return cfg == 2 ? 128 : 256; }
+
+}  // namespace qlq

@@ -157,23 +157,22 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
 
   // ---- split-K: publish, count arrivals, last one sums the slices in order
   if (S > 1) {
-    f32x4* part = reinterpret_cast<f32x4*>(a.partials);
-    store_partial(&part[((int64_t)s * a.NT + nt) * 64 + lane], tot);
+    const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
+    store_partial(part, ((int64_t)s * a.NT + nt) * 64 + lane, tot);
     wait_stores_performed();
     uint32_t prev = 0;
     if (lane == 0) prev = arrive(&a.counters[nt]);
     prev = __shfl(prev, 0, 64);
     if (prev != (uint32_t)(S - 1)) return;
+    // slices summed in order 0..S-1, whichever workgroup arrived last
     if constexpr (T::kIntAcc) {
       i32x4 t = {0, 0, 0, 0};
       for (int q = 0; q < S; ++q)
-        t += (q == s) ? __builtin_bit_cast(i32x4, tot)
-                      : __builtin_bit_cast(i32x4, load_partial(&part[((int64_t)q * a.NT + nt) * 64 + lane]));
+        t += __builtin_bit_cast(i32x4, load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane));
       tot = __builtin_bit_cast(f32x4, t);
     } else {
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < S; ++q)
-        t += (q == s) ? tot : load_partial(&part[((int64_t)q * a.NT + nt) * 64 + lane]);
+      for (int q = 0; q < S; ++q) t += load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane);
       tot = t;
     }
     if (lane == 0) reset_counter(&a.counters[nt]);

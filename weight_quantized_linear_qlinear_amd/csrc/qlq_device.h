@@ -140,23 +140,27 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 // Partial sums of one output tile, written by several workgroups, are read back
 // by the last one to arrive.  Workgroups of one launch may sit on different XCDs,
 // each with its own L2, so the partials travel through agent-coherent accesses
-// (64-bit atomic stores/loads at agent scope: the sc1 cache policy) instead of a
-// device-wide fence, which would write back and invalidate a whole L2 per
-// workgroup.  Order: partial stores -> wait until they are performed ->
-// increment the arrival counter (a device atomic).
+// (16-byte buffer stores and loads with the sc1 cache policy, write-through /
+// coherent across XCDs) instead of a device-wide fence, which would write back
+// and invalidate a whole L2 per workgroup.  Order: partial stores -> wait until
+// they are performed -> increment the arrival counter (a device atomic).
+// The buffer descriptor's record count is the partial region's size, so the
+// hardware range check drops any access outside it.
 
-__device__ __forceinline__ void store_partial(f32x4* p, f32x4 v) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  u32x4 b = __builtin_bit_cast(u32x4, v);
-  __hip_atomic_store(q, (uint64_t)b.x | ((uint64_t)b.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, (uint64_t)b.z | ((uint64_t)b.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kCachePolicySc1 = 16;       // sc1: coherent at agent scope
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufferWord3);
 }
 
-__device__ __forceinline__ f32x4 load_partial(const f32x4* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(f32x4, (u32x4){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
+// f32x4 index -> byte offset (the partial region is below 2^31 bytes)
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, int64_t idx, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)(idx * 16), 0, kCachePolicySc1);
+}
+
+__device__ __forceinline__ f32x4 load_partial(__amdgpu_buffer_rsrc_t r, int64_t idx) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(idx * 16), 0, kCachePolicySc1));
 }
 
 // Waits until this thread's earlier stores are performed (vmcnt = 0).

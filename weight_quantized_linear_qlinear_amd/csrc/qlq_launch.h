@@ -11,7 +11,9 @@ enum Scheme : int { kW8A16 = 0, kW8A8 = 1 };
 
 // How one GEMM call is cut into workgroups.
 struct GemmPlan {
-  int kind = 0;             // 0: small-M family (M <= 16), 1: large-M MFMA family
+  int kind = 0;             // 0: small-M family (M <= 16), 1: large-M register-staged
+                            // (any K), 2: large-M direct-to-LDS (K % 64 == 0)
+  int cfg = 0;              // kind 2: tile configuration (see gemm_mfma.hip)
   int S = 1;                // split-K factor (workgroups sharing one output tile)
   int units_per_split = 0;  // K units (64 or 128 inputs) per split
   int units_per_wave = 0;   // small-M: K units per wave
@@ -22,7 +24,8 @@ struct GemmPlan {
   size_t ws_counter_bytes = 0;
 };
 
-GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N);
+// `fast`: K % 64 == 0 and x 16-byte aligned (enables kind 2).
+GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool fast);
 
 // Arguments every GEMM kernel receives (plain pointers and sizes).
 struct GemmArgs {
@@ -33,6 +36,7 @@ struct GemmArgs {
   void* y;                  // bf16 [M,N], or int32/fp32 [M,N] accumulators
   uint32_t* counters;       // [tiles] arrival counters (split-K only)
   float* partials;          // split-K partial sums
+  uint32_t partials_bytes;  // size of the partial region
   int M, K, N, KT, NT;
   float input_scale;
   int out_acc;
@@ -43,6 +47,10 @@ hipError_t launch_gemm_small(int scheme, int qtype, const GemmPlan& plan, const 
                              hipStream_t st);
 hipError_t launch_gemm_large(int scheme, int qtype, const GemmPlan& plan, const GemmArgs& a,
                              hipStream_t st);
+hipError_t launch_gemm_mfma(int scheme, int qtype, const GemmPlan& plan, const GemmArgs& a,
+                            hipStream_t st);
+int mfma_cfg_tile_m(int cfg);
+int mfma_cfg_tile_n(int cfg);
 
 hipError_t launch_absmax_scale(const void* src, int is_bf16, int64_t numel, float qmax, float* out,
                                hipStream_t st);
