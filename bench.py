@@ -24,6 +24,8 @@ oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -54,6 +56,35 @@ def gemm_bytes(scheme, M, K, N, per_tensor):
 
 def act_quant_bytes(M, K):
     return 2 * M * K + M * K
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_gemm_mfma_int8_w8a16_stack.txt")
+
+
+def kernel_sources_hash():
+    """sha256 over the HIP sources (name + bytes, sorted): identifies the kernels a profile measured."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "weight_quantized_linear_qlinear_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(family):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE profile, or None when the
+    profile is for another kernel family or the kernels changed since it was taken."""
+    if family != ("int8_w8a16", "large") or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_PROFILE):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256") != kernel_sources_hash():
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
 
 
 def build_stack(qlq, synth, torch, dev, seed, layers):
@@ -128,6 +159,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=36, help="decoder layers in the stack (36 = the pages' config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run one 256 MiB device copy (known HBM bytes) so that "
+                         "profiler byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the quantized linear layer runs on a single MI355X here "
@@ -259,10 +293,11 @@ def main():
         achieved = g["bytes"] / g["launches"] / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 3)
-    roof["traffic"] = None
-    kernel_name = {("int8_w8a16", "large"): "gemm_large_kernel<int8, W8A16>",
-                   ("int8_w8a16", "small"): "gemm_small_kernel<int8, W8A16>",
-                   ("fp8_w8a8_static", "large"): "gemm_large_kernel<fp8, W8A8> + quant_act_kernel<fp8>",
+    roof["traffic"] = profiled_traffic(fam)
+    roof["algorithmic_bytes_per_launch"] = int(g["bytes"] / g["launches"])
+    kernel_name = {("int8_w8a16", "large"): "gemm_mfma_kernel<int8, W8A16, *> (M=256 and M=1024 launches)",
+                   ("int8_w8a16", "small"): "gemm_small_kernel<int8, W8A16> (M=1 and M=16 launches)",
+                   ("fp8_w8a8_static", "large"): "gemm_mfma_kernel<fp8, W8A8, *> + quant_act_kernel<fp8>",
                    ("fp8_w8a8_static", "small"): "gemm_small_kernel<fp8, W8A8> + quant_act_kernel<fp8>"}[fam]
     roof["kernel"] = kernel_name
     roof["avg_launch_us"] = round(avg_us, 3)
@@ -278,6 +313,13 @@ def main():
                        "layers": L, "M": list(Ms), "variants": [v[0] for v in VARIANTS],
                        "gemms_per_step": 3 * L * len(cases)},
             "cases": out_cases, "roofline": roof}
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 256 MiB read + 256 MiB written")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on its sample ...")
         layer0 = [synth.stack_weight(args.seed, 0, p, dev) for p in range(3)]
