@@ -2,6 +2,7 @@
 // Declarations and their contracts: include/qlq.h.
 #include "qlq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -71,31 +72,38 @@ namespace qlq {
 namespace {
 
 // Direct-to-LDS MFMA kernel: choose the tile configuration and split-K factor
-// that minimise the estimated makespan on 256 CUs.  Per-configuration figures
-// were measured on MI355X (time of one 64-input stage of one workgroup, and
-// workgroups resident per CU):
-//   cfg 0 (256 x 256): W8A16 2.84 us, W8A8 1.08 us, 1 per CU
-//   cfg 1 (128 x 256): W8A16 1.50 us, W8A8 0.90 us, 1 per CU
-//   cfg 2 (128 x 128): W8A16 1.08 us (1 per CU), W8A8 0.68 us (2 per CU)
-// Split-K adds its fp32/int32 partial traffic (written and read once each).
+// that minimise the estimated makespan on 256 CUs: rounds of resident
+// workgroups x (time per 64-input tile of K of one workgroup) plus, for
+// split-K, the partial traffic and the per-slice reduction round trips.  The
+// per-tile times were measured on MI355X with every CU busy (cold weights);
+// a lightly loaded GPU runs a tile up to ~15 % faster.
 GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
   constexpr int64_t kCUs = 256;
   const int64_t KT = cdiv(K, 64);
-  const double stage_us[2][3] = {{2.84, 1.50, 1.08}, {1.08, 0.90, 0.68}};
-  const int per_cu[2][3] = {{1, 1, 1}, {1, 1, 2}};
+  constexpr int kCfgs = 7;
+  // per 64-input tile of K (us): {W8A16, W8A8}, cfg 0..6 (cfg 3 is W8A8 only)
+  const double tile_us[2][kCfgs] = {{2.85, 1.51, 1.05, 0.0, 1.60, 1.23, 2.72},
+                                    {1.62, 0.86, 0.80, 1.61, 0.77, 0.57, 1.43}};
+  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1, 1}, {1, 1, 2, 1, 1, 1, 1}};
   const int sch = scheme == kW8A16 ? 0 : 1;
   GemmPlan best;
   double best_cost = 1e300;
-  for (int cfg = 0; cfg < 3; ++cfg) {
+  for (int cfg = 0; cfg < kCfgs && cfg < mfma_num_cfgs(); ++cfg) {
+    if (!mfma_cfg_valid(scheme, cfg)) continue;
+    const int64_t BKT = mfma_cfg_bkt(cfg);
+    if (KT % BKT != 0) continue;
+    const int64_t KS = KT / BKT;                                // LDS stages over K
     const int64_t BM = mfma_cfg_tile_m(cfg), BN = mfma_cfg_tile_n(cfg);
     const int64_t tiles = cdiv(M, BM) * cdiv(N, BN);
     for (int64_t S = 1; S <= 16; ++S) {
-      if (S > 1 && (tiles > kMaxSplitTiles || KT / S < 2)) break;
-      const int64_t ups = cdiv(KT, S);
-      if (cdiv(KT, ups) != S) continue;
-      const int64_t rounds = cdiv(tiles * S, kCUs * per_cu[sch][cfg]);
-      double cost = (double)rounds * ((double)ups * stage_us[sch][cfg] + 1.0);
-      if (S > 1) cost += (double)(S * tiles * BM * BN * 4 * 2) / 5.0e6 + 1.0;   // bytes / (5 TB/s), in us
+      if (S > 1 && (tiles > kMaxSplitTiles || KS / S < 2)) break;
+      const int64_t ups = cdiv(KS, S);
+      if (cdiv(KS, ups) != S) continue;
+      const int64_t slots = kCUs * per_cu[sch][cfg];
+      const int64_t rounds = cdiv(tiles * S, slots);
+      const double load = 0.85 + 0.15 * std::min(1.0, (double)(tiles * S) / (double)slots);
+      double cost = (double)rounds * ((double)(ups * BKT) * tile_us[sch][cfg] * load + 1.0);
+      if (S > 1) cost += (double)(S * tiles * BM * BN * 4 * 2) / 5.0e6 + 2.5 * (double)S;   // traffic + reduce
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = GemmPlan();

@@ -313,15 +313,13 @@ hipError_t launch_large_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) 
   using T = LargeTraits<QT, SCH>;
   constexpr int STAGE = (BM / 16 + BN / 16) * T::kBKT * T::kPlanes * 1024;
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-  if (a.fast) {
-    auto k = gemm_large_kernel<QT, SCH, BM, BN, true>;
-    hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
-    k<<<p.grid, 256, 2 * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
-  } else {
-    auto k = gemm_large_kernel<QT, SCH, BM, BN, false>;
-    hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
-    k<<<p.grid, 256, 2 * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
+  auto k = a.fast ? gemm_large_kernel<QT, SCH, BM, BN, true> : gemm_large_kernel<QT, SCH, BM, BN, false>;
+  static std::atomic<uint64_t> lds_set[2];       // per instantiation, per device
+  {
+    const hipError_t e = set_lds_limit((const void*)k, 2 * STAGE, lds_set[a.fast ? 1 : 0]);
+    if (e != hipSuccess) return e;
   }
+  k<<<p.grid, 256, 2 * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

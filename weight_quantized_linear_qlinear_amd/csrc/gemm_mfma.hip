@@ -32,6 +32,8 @@
 #include "qlq_device.h"
 #include "qlq_launch.h"
 
+#include <utility>
+
 namespace qlq {
 namespace {
 
@@ -62,14 +64,14 @@ struct MfmaTraits {
   static constexpr bool kIntAcc = (SCH == kW8A8 && QT == kInt8);
 };
 
-template <int QT, int SCH, int BM, int BN, int WM, int WN, int NSTAGE, bool SPLIT>
+template <int QT, int SCH, int BM, int BN, int WM, int WN, int BKT, int NSTAGE, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, int ups, int tiles_m, int tiles_n) {
   using T = MfmaTraits<QT, SCH>;
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static_assert(WAVES_M * WAVES_N == 4, "four waves");
   constexpr int TM = WM / 32, TN = WN / 32;                 // 32x32 blocks per wave
-  constexpr int A_FRAGS = (BM / 32) * T::kAFrags;            // per stage
-  constexpr int B_TILES = BN / 16;                           // packed tiles per stage
+  constexpr int A_FRAGS = (BM / 32) * T::kAFrags * BKT;      // per stage
+  constexpr int B_TILES = (BN / 16) * BKT;                   // packed tiles per stage
   constexpr int STAGE = (A_FRAGS + B_TILES) * 1024;
   constexpr int A_PER_WAVE = A_FRAGS / 4, B_PER_WAVE = B_TILES / 4;
   constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;             // DMA instructions per wave per stage
@@ -91,44 +93,49 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
   const int rest = logical / tiles_m;
   const int s = rest % S;
   const int tn = rest / S;
-  const int m0 = tm * BM, nt0 = tn * B_TILES;
+  const int m0 = tm * BM, nt0 = tn * (BN / 16);             // first 16-column weight tile
   const int tile_id = tn * tiles_m + tm;
 
   const int st_begin = s * ups;
   int st_end = st_begin + ups;
-  if (st_end > a.KT) st_end = a.KT;
+  const int KS = a.KT / BKT;                                 // stages over K (KT % BKT == 0)
+  if (st_end > KS) st_end = KS;
   const int nst = st_end - st_begin;
 
-  // ---- per-lane DMA source pointers (stage 0 of this slice); each stage adds 64 inputs
+  // ---- per-lane DMA source pointers (stage 0 of this slice); each stage adds 64 BKT inputs.
+  // A fragment f of a stage: f = (mb * BKT + kt) * kAFrags + q.
   const uint8_t* a_src[A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < A_PER_WAVE; ++i) {
     const int f = wave * A_PER_WAVE + i;                     // fragment index in the stage
-    const int mb = f / T::kAFrags, q = f % T::kAFrags;
+    const int mb = f / (T::kAFrags * BKT), kt = (f / T::kAFrags) % BKT, q = f % T::kAFrags;
     int row = m0 + mb * 32 + l32;
     row = row < a.M ? row : a.M - 1;                         // rows >= M: harmless duplicate
     int col;                                                 // element offset inside the stage
     if constexpr (SCH == kW8A16) col = (2 * (q >> 1) + kg) * 16 + (q & 1) * 8;      // (p, j) = (q/2, q%2)
     else if constexpr (QT == kInt8) col = (2 * q + kg) * 16;                         // step p = q
     else col = (2 * kg + q) * 16;                                                    // half h = q
-    a_src[i] = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)row * a.K + (int64_t)st_begin * kTileK + col) * T::kAElem;
+    a_src[i] = reinterpret_cast<const uint8_t*>(a.x) +
+               ((int64_t)row * a.K + ((int64_t)st_begin * BKT + kt) * kTileK + col) * T::kAElem;
   }
+  // B tile b of a stage: b = nb16 * BKT + kt (16-column block, 64-input tile)
   const uint8_t* b_src[B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < B_PER_WAVE; ++i) {
-    int ntile = nt0 + wave * B_PER_WAVE + i;
+    const int b = wave * B_PER_WAVE + i;
+    int ntile = nt0 + b / BKT;
     ntile = ntile < a.NT ? ntile : a.NT - 1;                 // columns >= N: harmless duplicate
-    b_src[i] = a.w + ((int64_t)ntile * a.KT + st_begin) * kTileBytes + lane * 16;
+    b_src[i] = a.w + ((int64_t)ntile * a.KT + (int64_t)st_begin * BKT + b % BKT) * kTileBytes + lane * 16;
   }
 
   auto issue = [&](int st_local, int slot) {
     uint8_t* base = smem + slot * STAGE;
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i)
-      dma16(a_src[i] + (int64_t)st_local * kTileK * T::kAElem, base + (wave * A_PER_WAVE + i) * 1024);
+      dma16(a_src[i] + (int64_t)st_local * BKT * kTileK * T::kAElem, base + (wave * A_PER_WAVE + i) * 1024);
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i)
-      dma16(b_src[i] + (int64_t)st_local * kTileBytes, base + (A_FRAGS + wave * B_PER_WAVE + i) * 1024);
+      dma16(b_src[i] + (int64_t)st_local * BKT * kTileBytes, base + (A_FRAGS + wave * B_PER_WAVE + i) * 1024);
   };
 
   // ---- per-lane column scales (W8A16)
@@ -152,67 +159,71 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
       acci[i][j] = (i32x16){};
     }
 
-  // B read offset of lane (column l32 of the wave's 32-column block, chunk c)
-  auto b_off = [&](int nb32, int c) {
+  // B read offset of lane (column l32 of the wave's 32-column block, 64-input tile kt, chunk c)
+  auto b_off = [&](int nb32, int kt, int c) {
     const int col = nb32 * 32 + l32;                          // column inside the workgroup tile
-    return (A_FRAGS + (col >> 4)) * 1024 + ((col & 15) + 16 * c) * 16;
+    return (A_FRAGS + (col >> 4) * BKT + kt) * 1024 + ((col & 15) + 16 * c) * 16;
   };
 
   auto compute = [&](const uint8_t* base) {
-    if constexpr (SCH == kW8A16) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        bf16x8 bfr[TN][2];
+    for (int kt = 0; kt < BKT; ++kt) {
+      if constexpr (SCH == kW8A16) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          u32x4 c = lds_read16(base + b_off(wn * TN + j, 2 * p + kg));
-          bfr[j][0] = dequant8<QT>(c.x, c.y, sc[j], sc_m128[j]);
-          bfr[j][1] = dequant8<QT>(c.z, c.w, sc[j], sc_m128[j]);
-        }
+        for (int p = 0; p < 2; ++p) {
+          bf16x8 bfr[TN][2];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+          for (int j = 0; j < TN; ++j) {
+            u32x4 c = lds_read16(base + b_off(wn * TN + j, kt, 2 * p + kg));
+            bfr[j][0] = dequant8<QT>(c.x, c.y, sc[j], sc_m128[j]);
+            bfr[j][1] = dequant8<QT>(c.z, c.w, sc[j], sc_m128[j]);
+          }
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const int f = (wm * TM + i) * T::kAFrags + 2 * p + jj;
-            bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + f * 1024 + lane * 16));
+          for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j][jj], accf[i][j], 0, 0, 0);
+            for (int i = 0; i < TM; ++i) {
+              const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + 2 * p + jj;
+              bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + f * 1024 + lane * 16));
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j][jj], accf[i][j], 0, 0, 0);
+            }
           }
         }
-      }
-    } else if constexpr (QT == kInt8) {
+      } else if constexpr (QT == kInt8) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        i32x4 bfr[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[j] = __builtin_bit_cast(i32x4, lds_read16(base + b_off(wn * TN + j, 2 * p + kg)));
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int f = (wm * TM + i) * T::kAFrags + p;
-          i32x4 af = __builtin_bit_cast(i32x4, lds_read16(base + f * 1024 + lane * 16));
+        for (int p = 0; p < 2; ++p) {
+          i32x4 bfr[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[j], acci[i][j], 0, 0, 0);
+            bfr[j] = __builtin_bit_cast(i32x4, lds_read16(base + b_off(wn * TN + j, kt, 2 * p + kg)));
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + p;
+            i32x4 af = __builtin_bit_cast(i32x4, lds_read16(base + f * 1024 + lane * 16));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[j], acci[i][j], 0, 0, 0);
+          }
         }
-      }
-    } else {
-      i32x8 bfr[TN];
+      } else {
+        i32x8 bfr[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        u32x4 c0 = lds_read16(base + b_off(wn * TN + j, 2 * kg));
-        u32x4 c1 = lds_read16(base + b_off(wn * TN + j, 2 * kg + 1));
-        bfr[j] = (i32x8){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
-      }
+        for (int j = 0; j < TN; ++j) {
+          u32x4 c0 = lds_read16(base + b_off(wn * TN + j, kt, 2 * kg));
+          u32x4 c1 = lds_read16(base + b_off(wn * TN + j, kt, 2 * kg + 1));
+          bfr[j] = (i32x8){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+        }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int f = (wm * TM + i) * T::kAFrags;
-        u32x4 a0 = lds_read16(base + f * 1024 + lane * 16);
-        u32x4 a1 = lds_read16(base + (f + 1) * 1024 + lane * 16);
-        i32x8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        for (int i = 0; i < TM; ++i) {
+          const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags;
+          u32x4 a0 = lds_read16(base + f * 1024 + lane * 16);
+          u32x4 a1 = lds_read16(base + (f + 1) * 1024 + lane * 16);
+          i32x8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bfr[j], accf[i][j], 0, 0, 0, 0, 0, 0);
+          for (int j = 0; j < TN; ++j)
+            accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bfr[j], accf[i][j], 0, 0, 0, 0, 0, 0);
+        }
       }
     }
   };
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
   // The loop body is branch-free: the prefetch source is clamped to the last
   // stage, so past the end it re-reads a valid stage into a slot nobody reads,
   // and every iteration waits for the same vmcnt.
-  constexpr int NMFMA = (SCH == kW8A16 ? 4 : (QT == kInt8 ? 2 : 1)) * TM * TN;
+  constexpr int NMFMA = (SCH == kW8A16 ? 4 : (QT == kInt8 ? 2 : 1)) * TM * TN * BKT;
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t) issue(t < nst ? t : nst - 1, t);
   for (int t = 0; t < nst; ++t) {
@@ -305,12 +316,18 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
   if (staged) {
     constexpr int PITCH = BN * 2 + 16;                       // bytes per staged row (padding spreads banks)
     constexpr int ROWS_FIT = (NSTAGE * STAGE) / PITCH;
-    constexpr int PASS_WM = (ROWS_FIT / WM) < WAVES_M ? (ROWS_FIT / WM) : WAVES_M;
-    static_assert(PASS_WM >= 1, "epilogue staging does not fit");
+    // Rows are staged in passes of whole 32-row blocks; block rb = wm * TM + i
+    // covers rows m0 + 32 rb .. + 31, so one pass is a contiguous row range.
+    constexpr int RB_ALL = BM / 32;
+    constexpr int RB_PASS = (ROWS_FIT / 32) < RB_ALL ? (ROWS_FIT / 32) : RB_ALL;
+    static_assert(RB_PASS >= 1, "epilogue staging does not fit");
     __syncthreads();                                         // every wave is done with the stage buffers
 #pragma unroll
-    for (int pass = 0; pass < WAVES_M; pass += PASS_WM) {
-      if (wm >= pass && wm < pass + PASS_WM) {
+    for (int pass = 0; pass < RB_ALL; pass += RB_PASS) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rb = wm * TM + i;
+        if (rb < pass || rb >= pass + RB_PASS) continue;     // wave-uniform
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int col = (wn * TN + j) * 32 + l32;
@@ -318,24 +335,22 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
           float comb = 1.0f;
           if (SCH == kW8A8) comb = n < a.N ? a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]) : 0.0f;
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int row = (wm - pass) * WM + i * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
-              float v;
-              if constexpr (SCH == kW8A16) v = accf[i][j][e];
-              else v = (T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e]) * comb;
-              *reinterpret_cast<__bf16*>(smem + row * PITCH + col * 2) = (__bf16)v;
-            }
+          for (int e = 0; e < 16; ++e) {
+            const int row = (rb - pass) * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
+            float v;
+            if constexpr (SCH == kW8A16) v = accf[i][j][e];
+            else v = (T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e]) * comb;
+            *reinterpret_cast<__bf16*>(smem + row * PITCH + col * 2) = (__bf16)v;
+          }
         }
       }
       __syncthreads();
       constexpr int CH = BN / 8;                             // 16-byte chunks per row
-      constexpr int ROWS = PASS_WM * WM;
+      const int ROWS = (RB_ALL - pass < RB_PASS ? RB_ALL - pass : RB_PASS) * 32;
 #pragma unroll 4
       for (int c = tid; c < ROWS * CH; c += 256) {
         const int row = c / CH, ch = c % CH;
-        const int m = m0 + pass * WM + row;
+        const int m = m0 + pass * 32 + row;
         const int n = nt0 * 16 + ch * 8;
         if (m < a.M && n < a.N) {
           u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * PITCH + ch * 16);
@@ -378,44 +393,76 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
   }
 }
 
-template <int QT, int SCH, int BM, int BN, int WM, int WN, int NSTAGE>
+template <int QT, int SCH, int BM, int BN, int WM, int WN, int BKT, int NSTAGE>
 hipError_t launch_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
   using T = MfmaTraits<QT, SCH>;
-  constexpr int STAGE = ((BM / 32) * T::kAFrags + BN / 16) * 1024;
+  constexpr int STAGE = ((BM / 32) * T::kAFrags + BN / 16) * BKT * 1024;
+  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-  auto k = p.S > 1 ? gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, NSTAGE, true>
-                   : gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, NSTAGE, false>;
-  static bool attr_set[2] = {false, false};     // one attribute call per instantiation
-  if (!attr_set[p.S > 1]) {
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * STAGE);
+  auto k = p.S > 1 ? gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, BKT, NSTAGE, true>
+                   : gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, BKT, NSTAGE, false>;
+  static std::atomic<uint64_t> lds_set[2];       // per instantiation, per device
+  {
+    const hipError_t e = set_lds_limit((const void*)k, NSTAGE * STAGE, lds_set[p.S > 1 ? 1 : 0]);
     if (e != hipSuccess) return e;
-    attr_set[p.S > 1] = true;
   }
   k<<<p.grid, 256, NSTAGE * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-}  // namespace
+// Tile configurations: workgroup tile BM x BN, per-wave WM x WN (four waves),
+// BKT 64-input tiles per LDS stage, NSTAGE stages.  One table feeds both the
+// dispatch below and the planner's queries.
+struct MfmaCfg {
+  int BM, BN, WM, WN, BKT, NSTAGE;
+  bool w8a16;   // instantiated for the weight-only scheme too (else W8A8 only)
+};
+constexpr MfmaCfg kMfmaCfgs[] = {
+    {256, 256, 128, 128, 1, 3, true},    // 0
+    {128, 256, 128, 64, 1, 4, true},     // 1
+    {128, 128, 64, 64, 1, 4, true},      // 2
+    {256, 256, 128, 128, 2, 2, false},   // 3
+    {128, 256, 128, 64, 2, 2, true},     // 4
+    {128, 128, 64, 64, 2, 3, true},      // 5
+    {256, 256, 256, 64, 1, 3, true},     // 6: each wave dequantizes only its own 64 columns
+};
+constexpr int kNumMfmaCfgs = sizeof(kMfmaCfgs) / sizeof(kMfmaCfgs[0]);
 
-// Tile configurations (BM x BN workgroup tile, WM x WN per wave, LDS stages).
-// cfg 0: 256 x 256, waves 2 x 2 of 128 x 128; cfg 1: 128 x 256, waves 1 x 4 of 128 x 64;
-// cfg 2: 128 x 128, waves 2 x 2 of 64 x 64.
-hipError_t launch_gemm_mfma(int scheme, int qtype, const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-#define QLQ_CFG(QT, SCH)                                                         \
-  switch (p.cfg) {                                                               \
-    case 0: return launch_t<QT, SCH, 256, 256, 128, 128, 3>(p, a, st);           \
-    case 1: return launch_t<QT, SCH, 128, 256, 128, 64, 4>(p, a, st);            \
-    default: return launch_t<QT, SCH, 128, 128, 64, 64, 4>(p, a, st);            \
-  }
-  if (scheme == kW8A16) {
-    if (qtype == kFp8) { QLQ_CFG(kFp8, kW8A16) } else { QLQ_CFG(kInt8, kW8A16) }
+template <int QT, int SCH, int C>
+hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  constexpr MfmaCfg c = kMfmaCfgs[C];
+  if constexpr (SCH == kW8A16 && !c.w8a16) {
+    return hipErrorInvalidValue;
   } else {
-    if (qtype == kFp8) { QLQ_CFG(kFp8, kW8A8) } else { QLQ_CFG(kInt8, kW8A8) }
+    return launch_t<QT, SCH, c.BM, c.BN, c.WM, c.WN, c.BKT, c.NSTAGE>(p, a, st);
   }
-#undef QLQ_CFG
 }
 
-int mfma_cfg_tile_m(int cfg) { return cfg == 0 ? 256 : 128; }
-int mfma_cfg_tile_n(int cfg) { return cfg == 2 ? 128 : 256; }
+template <int QT, int SCH, int... C>
+hipError_t dispatch_cfg(int cfg, const GemmPlan& p, const GemmArgs& a, hipStream_t st,
+                        std::integer_sequence<int, C...>) {
+  hipError_t r = hipErrorInvalidValue;
+  ((cfg == C ? (r = launch_cfg<QT, SCH, C>(p, a, st), 0) : 0), ...);
+  return r;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma(int scheme, int qtype, const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  const auto all = std::make_integer_sequence<int, kNumMfmaCfgs>{};
+  if (scheme == kW8A16)
+    return qtype == kFp8 ? dispatch_cfg<kFp8, kW8A16>(p.cfg, p, a, st, all)
+                         : dispatch_cfg<kInt8, kW8A16>(p.cfg, p, a, st, all);
+  return qtype == kFp8 ? dispatch_cfg<kFp8, kW8A8>(p.cfg, p, a, st, all)
+                       : dispatch_cfg<kInt8, kW8A8>(p.cfg, p, a, st, all);
+}
+
+int mfma_cfg_tile_m(int cfg) { return kMfmaCfgs[cfg].BM; }
+int mfma_cfg_tile_n(int cfg) { return kMfmaCfgs[cfg].BN; }
+int mfma_cfg_bkt(int cfg) { return kMfmaCfgs[cfg].BKT; }
+int mfma_num_cfgs() { return kNumMfmaCfgs; }
+bool mfma_cfg_valid(int scheme, int cfg) {
+  return cfg >= 0 && cfg < kNumMfmaCfgs && (scheme != kW8A16 || kMfmaCfgs[cfg].w8a16);
+}
 
 }  // namespace qlq

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -15,7 +16,7 @@ struct GemmPlan {
                             // (any K), 2: large-M direct-to-LDS (K % 64 == 0)
   int cfg = 0;              // kind 2: tile configuration (see gemm_mfma.hip)
   int S = 1;                // split-K factor (workgroups sharing one output tile)
-  int units_per_split = 0;  // K units (64 or 128 inputs) per split
+  int units_per_split = 0;  // K units per split (small-M: 64/128 inputs; kind 2: LDS stages)
   int units_per_wave = 0;   // small-M: K units per wave
   int BM = 0, BN = 0;       // large-M: workgroup tile
   int tiles = 0;            // output tiles (small: 16-column blocks)
@@ -51,6 +52,9 @@ hipError_t launch_gemm_mfma(int scheme, int qtype, const GemmPlan& plan, const G
                             hipStream_t st);
 int mfma_cfg_tile_m(int cfg);
 int mfma_cfg_tile_n(int cfg);
+int mfma_cfg_bkt(int cfg);
+int mfma_num_cfgs();
+bool mfma_cfg_valid(int scheme, int cfg);
 
 hipError_t launch_absmax_scale(const void* src, int is_bf16, int64_t numel, float qmax, float* out,
                                hipStream_t st);
@@ -58,5 +62,18 @@ hipError_t launch_pack_weight(const void* w, int is_bf16, int N, int K, int qtyp
                               uint8_t* packed, float* w_scale, hipStream_t st);
 hipError_t launch_unpack_weight(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st);
 hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st);
+
+// Raises kernel k's dynamic-LDS limit to `bytes` on the current device, once per
+// device (bit d of `done` records device d; devices past 63 set it every call).
+inline hipError_t set_lds_limit(const void* k, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+  return e;
+}
 
 }  // namespace qlq
