@@ -2,7 +2,6 @@
 // Declarations and their contracts: include/qlq.h.
 #include "qlq.h"
 
-#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -72,19 +71,21 @@ namespace qlq {
 namespace {
 
 // Direct-to-LDS MFMA kernel: choose the tile configuration and split-K factor
-// that minimise the estimated makespan on 256 CUs: rounds of resident
-// workgroups x (time per 64-input tile of K of one workgroup) plus, for
-// split-K, the partial traffic and the per-slice reduction round trips.  The
-// per-tile times were measured on MI355X with every CU busy (cold weights);
-// a lightly loaded GPU runs a tile up to ~15 % faster.
+// that minimise the estimated time on 256 CUs:
+//   rounds x (K stages per slice x t + e) + split-K (partial bytes x a + S x b),
+// where a round is one wave of resident workgroups.  t (per 64-input tile of K),
+// e (per round: prologue, epilogue, launch) and a, b were fitted to MI355X
+// timings of every (configuration, split) at the 3B-scale stack's shapes, M = 256
+// and 1024, with cold weights; the fit picks the fastest measured plan within 3 %.
 GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
   constexpr int64_t kCUs = 256;
   const int64_t KT = cdiv(K, 64);
-  constexpr int kCfgs = 7;
-  // per 64-input tile of K (us): {W8A16, W8A8}, cfg 0..6 (cfg 3 is W8A8 only)
-  const double tile_us[2][kCfgs] = {{2.85, 1.51, 1.05, 0.0, 1.60, 1.23, 2.72},
-                                    {1.62, 0.86, 0.80, 1.61, 0.77, 0.57, 1.43}};
-  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1, 1}, {1, 1, 2, 1, 1, 1, 1}};
+  constexpr int kCfgs = 6;
+  // {W8A16, W8A8} x cfg 0..5 (cfg 5 is W8A8 only)
+  const double t_us[2][kCfgs] = {{1.21, 0.87, 1.22, 0.91, 1.62, 0.0}, {0.85, 0.68, 0.61, 0.43, 1.10, 0.74}};
+  const double e_us[2][kCfgs] = {{3.8, 1.6, 3.7, 1.4, 9.7, 0.0}, {0.5, 0.5, 0.9, 0.5, 6.1, 6.0}};
+  const double a_us_per_mb[2] = {0.082, 0.129}, b_us[2] = {1.89, 2.18};
+  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1}, {1, 2, 1, 1, 1, 1}};
   const int sch = scheme == kW8A16 ? 0 : 1;
   GemmPlan best;
   double best_cost = 1e300;
@@ -95,15 +96,13 @@ GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
     const int64_t KS = KT / BKT;                                // LDS stages over K
     const int64_t BM = mfma_cfg_tile_m(cfg), BN = mfma_cfg_tile_n(cfg);
     const int64_t tiles = cdiv(M, BM) * cdiv(N, BN);
-    for (int64_t S = 1; S <= 16; ++S) {
+    for (int64_t S = 1; S <= 8; ++S) {
       if (S > 1 && (tiles > kMaxSplitTiles || KS / S < 2)) break;
       const int64_t ups = cdiv(KS, S);
       if (cdiv(KS, ups) != S) continue;
-      const int64_t slots = kCUs * per_cu[sch][cfg];
-      const int64_t rounds = cdiv(tiles * S, slots);
-      const double load = 0.85 + 0.15 * std::min(1.0, (double)(tiles * S) / (double)slots);
-      double cost = (double)rounds * ((double)(ups * BKT) * tile_us[sch][cfg] * load + 1.0);
-      if (S > 1) cost += (double)(S * tiles * BM * BN * 4 * 2) / 5.0e6 + 2.5 * (double)S;   // traffic + reduce
+      const int64_t rounds = cdiv(tiles * S, kCUs * per_cu[sch][cfg]);
+      double cost = (double)rounds * ((double)(ups * BKT) * t_us[sch][cfg] + e_us[sch][cfg]);
+      if (S > 1) cost += (double)(S * tiles * BM * BN * 8) * 1e-6 * a_us_per_mb[sch] + b_us[sch] * (double)S;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = GemmPlan();

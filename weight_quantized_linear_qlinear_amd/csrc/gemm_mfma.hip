@@ -16,10 +16,14 @@
 //    interleaved between the MFMAs (sched_group_barrier);
 //  * the bf16 output tile is staged through LDS so global stores are whole
 //    16-byte chunks of rows;
-//  * A fragments land in LDS in MFMA lane order (each lane fetches its own 16
-//    bytes of x), B is the packed weight tile copied verbatim and read with
-//    per-lane addresses; every ds_read_b128 of a wave covers contiguous 128-byte
-//    groups, so there are no bank conflicts;
+//  * x rows that fill whole 128-byte lines per stage (bf16 x; 8-bit x with two
+//    64-input tiles per stage) land in LDS row-major with the 16-byte chunks of
+//    each line XOR-swizzled by the row, so every DMA instruction fetches 8 whole
+//    lines (the vector L1 keeps a fixed number of requests in flight per CU, so
+//    bytes per request set the streaming rate) and the MFMA reads hit distinct
+//    banks; otherwise A fragments land in MFMA lane order.  B is the packed
+//    weight tile copied verbatim (8 whole lines per instruction) and read with
+//    per-lane addresses;
 //  * W8A16 dequantizes B in registers right after the LDS read:
 //    bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
 //  * large per-wave tiles (128 x 64 or 128 x 128) keep LDS traffic within budget.
@@ -65,17 +69,24 @@ struct MfmaTraits {
 };
 
 template <int QT, int SCH, int BM, int BN, int WM, int WN, int BKT, int NSTAGE, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, int ups, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kernel(GemmArgs a, int S, int ups, int tiles_m,
+                                                                                 int tiles_n) {
   using T = MfmaTraits<QT, SCH>;
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static_assert(WAVES_M * WAVES_N == 4, "four waves");
+  constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;         // waves, threads
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int TM = WM / 32, TN = WN / 32;                 // 32x32 blocks per wave
   constexpr int A_FRAGS = (BM / 32) * T::kAFrags * BKT;      // per stage
   constexpr int B_TILES = (BN / 16) * BKT;                   // packed tiles per stage
   constexpr int STAGE = (A_FRAGS + B_TILES) * 1024;
-  constexpr int A_PER_WAVE = A_FRAGS / 4, B_PER_WAVE = B_TILES / 4;
+  constexpr int A_PER_WAVE = A_FRAGS / NW, B_PER_WAVE = B_TILES / NW;
+  constexpr int ROW_BYTES = kTileK * BKT * T::kAElem;        // bytes of one x row per stage
+  constexpr bool LINE_A = ROW_BYTES >= 128;
+  constexpr int LINES = ROW_BYTES / 128;
+  static_assert(!LINE_A || (ROW_BYTES % 128 == 0 && A_FRAGS * 8 == BM * LINES), "A line layout");
+  static_assert(LINE_A || SCH == kW8A8, "bf16 x always fills whole lines");
   constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;             // DMA instructions per wave per stage
-  static_assert(A_FRAGS % 4 == 0 && B_TILES % 4 == 0, "DMA split");
+  static_assert(A_FRAGS % NW == 0 && B_TILES % NW == 0, "DMA split");
   static_assert(LOADS * (NSTAGE - 2) < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -103,20 +114,34 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
   const int nst = st_end - st_begin;
 
   // ---- per-lane DMA source pointers (stage 0 of this slice); each stage adds 64 BKT inputs.
-  // A fragment f of a stage: f = (mb * BKT + kt) * kAFrags + q.
+  // LINE_A (an x row of a stage spans whole 128-byte lines): the stage holds x
+  // row-major, [row][line][8 chunks of 16 bytes], chunk c of row r stored at
+  // position c ^ (r % 8) within its line.  One DMA instruction then fetches 8
+  // whole lines (one request per line), and the MFMA reads below stay free of
+  // bank conflicts.  Otherwise (8-bit x, one 64-input tile per stage) A fragment
+  // f of a stage is f = (mb * BKT + kt) * kAFrags + q, in MFMA lane order.
   const uint8_t* a_src[A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < A_PER_WAVE; ++i) {
-    const int f = wave * A_PER_WAVE + i;                     // fragment index in the stage
-    const int mb = f / (T::kAFrags * BKT), kt = (f / T::kAFrags) % BKT, q = f % T::kAFrags;
-    int row = m0 + mb * 32 + l32;
-    row = row < a.M ? row : a.M - 1;                         // rows >= M: harmless duplicate
-    int col;                                                 // element offset inside the stage
-    if constexpr (SCH == kW8A16) col = (2 * (q >> 1) + kg) * 16 + (q & 1) * 8;      // (p, j) = (q/2, q%2)
-    else if constexpr (QT == kInt8) col = (2 * q + kg) * 16;                         // step p = q
-    else col = (2 * kg + q) * 16;                                                    // half h = q
-    a_src[i] = reinterpret_cast<const uint8_t*>(a.x) +
-               ((int64_t)row * a.K + ((int64_t)st_begin * BKT + kt) * kTileK + col) * T::kAElem;
+    const int f = wave * A_PER_WAVE + i;                     // DMA instruction index in the stage
+    if constexpr (LINE_A) {
+      const int slot = f * 8 + (lane >> 3);                  // (row, line) slot, row-major
+      const int r = slot / LINES, line = slot % LINES;
+      const int c = (lane & 7) ^ (r & 7);
+      int row = m0 + r;
+      row = row < a.M ? row : a.M - 1;                       // rows >= M: harmless duplicate
+      a_src[i] = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)row * a.K + (int64_t)st_begin * BKT * kTileK) * T::kAElem +
+                 line * 128 + c * 16;
+    } else {
+      const int mb = f / (T::kAFrags * BKT), kt = (f / T::kAFrags) % BKT, q = f % T::kAFrags;
+      int row = m0 + mb * 32 + l32;
+      row = row < a.M ? row : a.M - 1;
+      int col;                                               // element offset inside the stage
+      if constexpr (QT == kInt8) col = (2 * q + kg) * 16;    // step p = q
+      else col = (2 * kg + q) * 16;                          // half h = q
+      a_src[i] = reinterpret_cast<const uint8_t*>(a.x) +
+                 ((int64_t)row * a.K + ((int64_t)st_begin * BKT + kt) * kTileK + col) * T::kAElem;
+    }
   }
   // B tile b of a stage: b = nb16 * BKT + kt (16-column block, 64-input tile)
   const uint8_t* b_src[B_PER_WAVE];
@@ -165,6 +190,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
     return (A_FRAGS + (col >> 4) * BKT + kt) * 1024 + ((col & 15) + 16 * c) * 16;
   };
 
+  // LINE_A read offset of lane's row in row block i of this wave, 16-byte chunk c of the stage row
+  auto a_off = [&](int i, int c) {
+    const int r = (wm * TM + i) * 32 + l32;
+    return (r * LINES + (c >> 3)) * 128 + (((c & 7) ^ (l32 & 7)) << 4);
+  };
+
   auto compute = [&](const uint8_t* base) {
 #pragma unroll
     for (int kt = 0; kt < BKT; ++kt) {
@@ -182,8 +213,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
           for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-              const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + 2 * p + jj;
-              bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + f * 1024 + lane * 16));
+              bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + a_off(i, kt * 8 + 4 * p + 2 * kg + jj)));
 #pragma unroll
               for (int j = 0; j < TN; ++j)
                 accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j][jj], accf[i][j], 0, 0, 0);
@@ -199,8 +229,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
             bfr[j] = __builtin_bit_cast(i32x4, lds_read16(base + b_off(wn * TN + j, kt, 2 * p + kg)));
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
-            const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + p;
-            i32x4 af = __builtin_bit_cast(i32x4, lds_read16(base + f * 1024 + lane * 16));
+            i32x4 af;
+            if constexpr (LINE_A) {
+              af = __builtin_bit_cast(i32x4, lds_read16(base + a_off(i, kt * 4 + 2 * p + kg)));
+            } else {
+              const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + p;
+              af = __builtin_bit_cast(i32x4, lds_read16(base + f * 1024 + lane * 16));
+            }
 #pragma unroll
             for (int j = 0; j < TN; ++j)
               acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[j], acci[i][j], 0, 0, 0);
@@ -216,9 +251,15 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags;
-          u32x4 a0 = lds_read16(base + f * 1024 + lane * 16);
-          u32x4 a1 = lds_read16(base + (f + 1) * 1024 + lane * 16);
+          u32x4 a0, a1;
+          if constexpr (LINE_A) {
+            a0 = lds_read16(base + a_off(i, kt * 4 + 2 * kg));
+            a1 = lds_read16(base + a_off(i, kt * 4 + 2 * kg + 1));
+          } else {
+            const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags;
+            a0 = lds_read16(base + f * 1024 + lane * 16);
+            a1 = lds_read16(base + (f + 1) * 1024 + lane * 16);
+          }
           i32x8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
           for (int j = 0; j < TN; ++j)
@@ -265,13 +306,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
   };
   if constexpr (SPLIT) {
     const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
-    const int64_t mine = ((int64_t)s * tiles_m * tiles_n + tile_id) * NV * 256;
+    const int64_t mine = ((int64_t)s * tiles_m * tiles_n + tile_id) * NV * NT;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) store_partial(part, mine + ((i * TN + j) * 4 + v) * 256 + tid, acc_vec(i, j, v));
+        for (int v = 0; v < 4; ++v) store_partial(part, mine + ((i * TN + j) * 4 + v) * NT + tid, acc_vec(i, j, v));
     wait_stores_performed();
     __shared__ uint32_t s_prev;
     __syncthreads();
@@ -281,8 +322,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
     // Sum the slices in slice order 0..S-1 (independent of which workgroup
     // arrived last, so the fp32 result is deterministic); each slice's values
     // are loaded together, straight into the accumulator registers.
-    const int64_t slice = (int64_t)tiles_m * tiles_n * NV * 256;
-    const int64_t base = (int64_t)tile_id * NV * 256;
+    const int64_t slice = (int64_t)tiles_m * tiles_n * NV * NT;
+    const int64_t base = (int64_t)tile_id * NV * NT;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -297,7 +338,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const f32x4 p = load_partial(part, base + q * slice + ((i * TN + j) * 4 + v) * 256 + tid);
+            const f32x4 p = load_partial(part, base + q * slice + ((i * TN + j) * 4 + v) * NT + tid);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if constexpr (T::kIntAcc) acci[i][j][4 * v + e] += __builtin_bit_cast(i32x4, p)[e];
@@ -348,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a, int S, in
       constexpr int CH = BN / 8;                             // 16-byte chunks per row
       const int ROWS = (RB_ALL - pass < RB_PASS ? RB_ALL - pass : RB_PASS) * 32;
 #pragma unroll 4
-      for (int c = tid; c < ROWS * CH; c += 256) {
+      for (int c = tid; c < ROWS * CH; c += NT) {
         const int row = c / CH, ch = c % CH;
         const int m = m0 + pass * 32 + row;
         const int n = nt0 * 16 + ch * 8;
@@ -406,11 +447,11 @@ hipError_t launch_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
     const hipError_t e = set_lds_limit((const void*)k, NSTAGE * STAGE, lds_set[p.S > 1 ? 1 : 0]);
     if (e != hipSuccess) return e;
   }
-  k<<<p.grid, 256, NSTAGE * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
+  k<<<p.grid, (BM / WM) * (BN / WN) * 64, NSTAGE * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-// Tile configurations: workgroup tile BM x BN, per-wave WM x WN (four waves),
+// Tile configurations: workgroup tile BM x BN, per-wave WM x WN (four or eight waves),
 // BKT 64-input tiles per LDS stage, NSTAGE stages.  One table feeds both the
 // dispatch below and the planner's queries.
 struct MfmaCfg {
@@ -418,13 +459,12 @@ struct MfmaCfg {
   bool w8a16;   // instantiated for the weight-only scheme too (else W8A8 only)
 };
 constexpr MfmaCfg kMfmaCfgs[] = {
-    {256, 256, 128, 128, 1, 3, true},    // 0
-    {128, 256, 128, 64, 1, 4, true},     // 1
-    {128, 128, 64, 64, 1, 4, true},      // 2
-    {256, 256, 128, 128, 2, 2, false},   // 3
-    {128, 256, 128, 64, 2, 2, true},     // 4
-    {128, 128, 64, 64, 2, 3, true},      // 5
-    {256, 256, 256, 64, 1, 3, true},     // 6: each wave dequantizes only its own 64 columns
+    {128, 256, 128, 64, 1, 4, true},     // 0
+    {128, 128, 64, 64, 1, 4, true},      // 1
+    {128, 256, 128, 64, 2, 2, true},     // 2
+    {128, 128, 64, 64, 2, 3, true},      // 3
+    {256, 256, 128, 64, 1, 3, true},     // 4: eight waves, two per SIMD
+    {256, 256, 128, 64, 2, 2, false},    // 5: eight waves (bf16 x would need 192 KiB of LDS)
 };
 constexpr int kNumMfmaCfgs = sizeof(kMfmaCfgs) / sizeof(kMfmaCfgs[0]);
 
