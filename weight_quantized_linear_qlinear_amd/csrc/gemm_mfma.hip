@@ -60,6 +60,9 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
 
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// four fp32 -> four bf16 (RNE), first value in the lowest bytes
+__device__ __forceinline__ u32x2 pack_bf16x4(f32x4 v) { return (u32x2){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}; }
+
 template <int QT, int SCH>
 struct MfmaTraits {
   static constexpr int kAElem = SCH == kW8A16 ? 2 : 1;       // bytes per x element
@@ -67,6 +70,15 @@ struct MfmaTraits {
   static constexpr int kAFrags = SCH == kW8A16 ? 4 : 2;
   static constexpr bool kIntAcc = (SCH == kW8A8 && QT == kInt8);
 };
+
+// Dynamic LDS of one workgroup: the stage ring, or the staged bf16 output tile
+// if that is larger (it reuses the ring after the main loop).
+template <int QT, int SCH, int BM, int BN, int BKT, int NSTAGE>
+constexpr int kLdsBytes() {
+  constexpr int stage = ((BM / 32) * MfmaTraits<QT, SCH>::kAFrags + BN / 16) * BKT * 1024;
+  constexpr int ring = NSTAGE * stage, out = BM * (BN * 2 + 16);
+  return ring > out ? ring : out;
+}
 
 template <int QT, int SCH, int BM, int BN, int WM, int WN, int BKT, int NSTAGE, bool SPLIT>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kernel(GemmArgs a, int S, int ups, int tiles_m,
@@ -174,6 +186,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     sc_m128[j] = -128.0f * v;
   }
 
+  // W8A8 per-tensor combined scale s_x * s_w, loaded before the main loop
+  const float comb_t = (SCH == kW8A8 && a.scale_per_tensor) ? a.input_scale * a.w_scale[0] : 1.0f;
+
   f32x16 accf[TM][TN];
   i32x16 acci[TM][TN];
 #pragma unroll
@@ -216,7 +231,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
               bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + a_off(i, kt * 8 + 4 * p + 2 * kg + jj)));
 #pragma unroll
               for (int j = 0; j < TN; ++j)
-                accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j][jj], accf[i][j], 0, 0, 0);
+                accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j][jj], af, accf[i][j], 0, 0, 0);
             }
           }
         }
@@ -238,7 +253,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[j], acci[i][j], 0, 0, 0);
+              acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfr[j], af, acci[i][j], 0, 0, 0);
           }
         }
       } else {
@@ -263,7 +278,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
           i32x8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bfr[j], accf[i][j], 0, 0, 0, 0, 0, 0);
+            accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af, accf[i][j], 0, 0, 0, 0, 0, 0);
         }
       }
     }
@@ -349,76 +364,80 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     if (tid == 0) reset_counter(&a.counters[tile_id]);
   }
 
-  // ---- epilogue.  bf16 outputs go through LDS so that global stores are whole
-  // 16-byte row chunks (a wave writes 1 KiB of contiguous rows); accumulator
-  // outputs and rows that are not 16-byte aligned are stored element by element.
-  // 32x32 block (i, j): lane holds column l32, value e at row 8 (e / 4) + 4 kg + (e % 4).
+  // ---- epilogue.  The MFMAs take the weights as their first operand, so block
+  // (i, j) holds the transposed product: lane l has output row l32 of block i and,
+  // for value e, column 8 (e / 4) + 4 kg + (e % 4) of block j, i.e. four
+  // consecutive columns per group of four values.  bf16 outputs go through LDS
+  // (8-byte writes) so that global stores are whole 16-byte chunks of rows;
+  // accumulator outputs and rows that are not 16-byte aligned are stored directly.
   const bool staged = !(SCH == kW8A8 && a.out_acc) && (a.N % 8 == 0);
   if (staged) {
     constexpr int PITCH = BN * 2 + 16;                       // bytes per staged row (padding spreads banks)
-    constexpr int ROWS_FIT = (NSTAGE * STAGE) / PITCH;
-    // Rows are staged in passes of whole 32-row blocks; block rb = wm * TM + i
-    // covers rows m0 + 32 rb .. + 31, so one pass is a contiguous row range.
-    constexpr int RB_ALL = BM / 32;
-    constexpr int RB_PASS = (ROWS_FIT / 32) < RB_ALL ? (ROWS_FIT / 32) : RB_ALL;
-    static_assert(RB_PASS >= 1, "epilogue staging does not fit");
+    static_assert(BM * PITCH <= kLdsBytes<QT, SCH, BM, BN, BKT, NSTAGE>(), "staging fits the LDS allocation");
     __syncthreads();                                         // every wave is done with the stage buffers
+    // W8A8 combined scales s_x * s_w[n] for this lane's 4 TN groups of four columns
+    // (all loads issued before the first use; N % 8 == 0 here, so n < N implies n + 3 < N)
+    f32x4 comb[TN][4];
 #pragma unroll
-    for (int pass = 0; pass < RB_ALL; pass += RB_PASS) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int rb = wm * TM + i;
-        if (rb < pass || rb >= pass + RB_PASS) continue;     // wave-uniform
+      for (int g = 0; g < 4; ++g) {
+        comb[j][g] = (f32x4){comb_t, comb_t, comb_t, comb_t};
+        if (SCH == kW8A8 && !a.scale_per_tensor) {
+          const int n = nt0 * 16 + (wn * TN + j) * 32 + 8 * g + 4 * kg;
+          if (n < a.N) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = (wn * TN + j) * 32 + l32;
-          const int n = nt0 * 16 + col;
-          float comb = 1.0f;
-          if (SCH == kW8A8) comb = n < a.N ? a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]) : 0.0f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = (rb - pass) * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
-            float v;
-            if constexpr (SCH == kW8A16) v = accf[i][j][e];
-            else v = (T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e]) * comb;
-            *reinterpret_cast<__bf16*>(smem + row * PITCH + col * 2) = (__bf16)v;
+            for (int c = 0; c < 4; ++c) comb[j][g][c] = a.input_scale * a.w_scale[n + c];
           }
         }
       }
-      __syncthreads();
-      constexpr int CH = BN / 8;                             // 16-byte chunks per row
-      const int ROWS = (RB_ALL - pass < RB_PASS ? RB_ALL - pass : RB_PASS) * 32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = (wn * TN + j) * 32 + 8 * g + 4 * kg;  // first of this lane's four columns
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          f32x4 v;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if constexpr (SCH == kW8A16) v[c] = accf[i][j][4 * g + c];
+            else v[c] = (T::kIntAcc ? (float)acci[i][j][4 * g + c] : accf[i][j][4 * g + c]) * comb[j][g][c];
+          }
+          const int row = (wm * TM + i) * 32 + l32;
+          *reinterpret_cast<u32x2*>(smem + row * PITCH + col * 2) = pack_bf16x4(v);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CH = BN / 8;                               // 16-byte chunks per row
 #pragma unroll 4
-      for (int c = tid; c < ROWS * CH; c += NT) {
-        const int row = c / CH, ch = c % CH;
-        const int m = m0 + pass * 32 + row;
-        const int n = nt0 * 16 + ch * 8;
-        if (m < a.M && n < a.N) {
-          u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * PITCH + ch * 16);
-          __bf16* dst = reinterpret_cast<__bf16*>(a.y) + (int64_t)m * a.N + n;
-          if (n + 8 <= a.N) {
-            st16(dst, v);
-          } else {
-            const __bf16* src = reinterpret_cast<const __bf16*>(&v);
-            for (int e = 0; e < a.N - n; ++e) dst[e] = src[e];
-          }
+    for (int c = tid; c < BM * CH; c += NT) {
+      const int row = c / CH, ch = c % CH;
+      const int m = m0 + row;
+      const int n = nt0 * 16 + ch * 8;
+      if (m < a.M && n < a.N) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * PITCH + ch * 16);
+        __bf16* dst = reinterpret_cast<__bf16*>(a.y) + (int64_t)m * a.N + n;
+        if (n + 8 <= a.N) {
+          st16(dst, v);
+        } else {
+          const __bf16* src = reinterpret_cast<const __bf16*>(&v);
+          for (int e = 0; e < a.N - n; ++e) dst[e] = src[e];
         }
       }
-      __syncthreads();
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = nt0 * 16 + (wn * TN + j) * 32 + l32;
-      if (n >= a.N) continue;
-      float comb = 0.0f;
-      if (SCH == kW8A8 && !a.out_acc) comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + (wm * TM + i) * 32 + l32;
+      if (m >= a.M) continue;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
-          if (m >= a.M) continue;
+          const int n = nt0 * 16 + (wn * TN + j) * 32 + 8 * (e >> 2) + 4 * kg + (e & 3);
+          if (n >= a.N) continue;
           const int64_t o = (int64_t)m * a.N + n;
           if constexpr (SCH == kW8A16) {
             reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)accf[i][j][e];
@@ -426,6 +445,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
             if constexpr (T::kIntAcc) reinterpret_cast<int32_t*>(a.y)[o] = acci[i][j][e];
             else reinterpret_cast<float*>(a.y)[o] = accf[i][j][e];
           } else {
+            const float comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
             const float v = T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e];
             reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
           }
@@ -436,18 +456,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 
 template <int QT, int SCH, int BM, int BN, int WM, int WN, int BKT, int NSTAGE>
 hipError_t launch_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-  using T = MfmaTraits<QT, SCH>;
-  constexpr int STAGE = ((BM / 32) * T::kAFrags + BN / 16) * BKT * 1024;
-  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
+  constexpr int LDS = kLdsBytes<QT, SCH, BM, BN, BKT, NSTAGE>();
+  static_assert(LDS <= 160 * 1024, "LDS");
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   auto k = p.S > 1 ? gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, BKT, NSTAGE, true>
                    : gemm_mfma_kernel<QT, SCH, BM, BN, WM, WN, BKT, NSTAGE, false>;
   static std::atomic<uint64_t> lds_set[2];       // per instantiation, per device
   {
-    const hipError_t e = set_lds_limit((const void*)k, NSTAGE * STAGE, lds_set[p.S > 1 ? 1 : 0]);
+    const hipError_t e = set_lds_limit((const void*)k, LDS, lds_set[p.S > 1 ? 1 : 0]);
     if (e != hipSuccess) return e;
   }
-  k<<<p.grid, (BM / WM) * (BN / WN) * 64, NSTAGE * STAGE, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
+  k<<<p.grid, (BM / WM) * (BN / WN) * 64, LDS, st>>>(a, p.S, p.units_per_split, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -497,9 +516,9 @@ hipError_t launch_gemm_mfma(int scheme, int qtype, const GemmPlan& p, const Gemm
                        : dispatch_cfg<kInt8, kW8A8>(p.cfg, p, a, st, all);
 }
 
-int mfma_cfg_tile_m(int cfg) { return kMfmaCfgs[cfg].BM; }
-int mfma_cfg_tile_n(int cfg) { return kMfmaCfgs[cfg].BN; }
-int mfma_cfg_bkt(int cfg) { return kMfmaCfgs[cfg].BKT; }
+int mfma_cfg_tile_m(int cfg) { return cfg >= 0 && cfg < kNumMfmaCfgs ? kMfmaCfgs[cfg].BM : 0; }
+int mfma_cfg_tile_n(int cfg) { return cfg >= 0 && cfg < kNumMfmaCfgs ? kMfmaCfgs[cfg].BN : 0; }
+int mfma_cfg_bkt(int cfg) { return cfg >= 0 && cfg < kNumMfmaCfgs ? kMfmaCfgs[cfg].BKT : 1; }
 int mfma_num_cfgs() { return kNumMfmaCfgs; }
 bool mfma_cfg_valid(int scheme, int cfg) {
   return cfg >= 0 && cfg < kNumMfmaCfgs && (scheme != kW8A16 || kMfmaCfgs[cfg].w8a16);
