@@ -21,7 +21,8 @@ Sources ("the pages"):
   support): scheme table (int8_w8a16 / int8_w8a8_static) and key-design list
   (W8A16 dequantizes int8 weights to BF16 for a standard matmul; W8A8 static
   quantizes activations at run time with one fixed, offline-calibrated scalar
-  per layer and runs an INT8 GEMM with int32 accumulation).
+  per layer and runs an INT8 GEMM with int32 accumulation; the per-token
+  absmax alternative it contrasts with is the dynamic scheme here).
 * "tiny-vLLM" README, section "Quantization Results" / "Quality Check":
   reconstruction error of the quantized weights (relative L2, cosine).
 
@@ -34,14 +35,15 @@ to a tolerance there.
 from .codecs import (bf16_bits_to_f32, f32_to_bf16_bits, bf16_round,
                      e4m3fn_decode, e4m3fn_encode_sat, E4M3FN_MAX, INT8_QMAX)
 from .qlinear import (qmax_of, weight_scale, quantize_weight, dequantize_weight_bf16,
-                      calibrate_input_scale, quantize_act_static, qlinear_w8a16,
-                      w8a8_accumulate, w8a8_epilogue, qlinear_w8a8_static,
-                      reconstruction_error)
+                      calibrate_input_scale, quantize_act_static, quantize_act_dynamic,
+                      qlinear_w8a16, w8a8_accumulate, w8a8_epilogue, qlinear_w8a8_static,
+                      w8a8_epilogue_per_token, qlinear_w8a8_dynamic, reconstruction_error)
 
 __all__ = [
     "bf16_bits_to_f32", "f32_to_bf16_bits", "bf16_round", "e4m3fn_decode",
     "e4m3fn_encode_sat", "E4M3FN_MAX", "INT8_QMAX", "qmax_of", "weight_scale",
     "quantize_weight", "dequantize_weight_bf16", "calibrate_input_scale",
-    "quantize_act_static", "qlinear_w8a16", "w8a8_accumulate", "w8a8_epilogue",
-    "qlinear_w8a8_static", "reconstruction_error",
+    "quantize_act_static", "quantize_act_dynamic", "qlinear_w8a16", "w8a8_accumulate",
+    "w8a8_epilogue", "qlinear_w8a8_static", "w8a8_epilogue_per_token", "qlinear_w8a8_dynamic",
+    "reconstruction_error",
 ]

@@ -1,5 +1,6 @@
-"""Oracle quantized linear layer: weight quantizer, static activation quantizer,
-W8A16 and W8A8-static GEMMs with their epilogues.
+"""Oracle quantized linear layer: weight quantizer, static and dynamic (per-token)
+activation quantizers, W8A16, W8A8-static and W8A8-dynamic GEMMs with their
+epilogues.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -21,7 +22,15 @@ Readings where the pages are silent (each is listed in the design doc):
   and then to bf16;
 * W8A8 INT8 accumulates exactly (int32 on the device); W8A8 FP8 accumulates
   exactly here and is rounded once to fp32; the epilogue is
-  y = bf16(fp32(acc) * fp32(s_x * s_w[n])), the combined scale formed in fp32.
+  y = bf16(fp32(acc) * fp32(s_x * s_w[n])), the combined scale formed in fp32;
+* dynamic per-token activation quantization ("Nano-vLLM-MOE" README mirror,
+  section "INT8 量化支持", key-design list: the W8A8 static bullet names the
+  per-token absmax variant whose extra run-time reduce static scaling avoids)
+  uses, for every row m, the weight
+  quantizer's rule on that row alone: s_x[m] = absmax(x[m, :]) / qmax (1.0
+  for an all-zero row) and xq = sat(RNE(x / s_x[m])); its epilogue is the
+  static one with s_x replaced by s_x[m]:
+  y = bf16(fp32(acc) * fp32(s_x[m] * s_w[n])).
 """
 from __future__ import annotations
 
@@ -108,6 +117,19 @@ def quantize_act_static(x_bf16: np.ndarray, input_scale, qtype: str) -> np.ndarr
     return _encode((xf / np.float32(input_scale)).astype(np.float32), qtype)
 
 
+def quantize_act_dynamic(x_bf16: np.ndarray, qtype: str):
+    """Per-token (per-row) dynamic quantization of x[M, K].
+
+    Row m gets s_x[m] = fp32(absmax(x[m, :])) / qmax (1.0 if the row is all
+    zero) and codes xq[m, k] = sat(RNE(x[m, k] / s_x[m])).
+    Returns (codes [M, K] int8 or uint8 e4m3fn, scales fp32 [M]).
+    """
+    xf = bf16_bits_to_f32(x_bf16)
+    s = weight_scale(np.abs(xf).max(axis=1), qtype)           # [M]
+    q = _encode((xf / s[:, None]).astype(np.float32), qtype)
+    return q, s
+
+
 def qlinear_w8a16(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray,
                   qtype: str) -> np.ndarray:
     """Weight-only quantized linear: y = bf16(fp32(sum_k x[m,k] * wd[n,k])), bf16 bits [M, N]."""
@@ -155,6 +177,26 @@ def qlinear_w8a8_static(xq: np.ndarray, input_scale, codes: np.ndarray, scales: 
             return acc.astype(np.int32)
         return acc
     return w8a8_epilogue(acc, input_scale, scales)
+
+
+def w8a8_epilogue_per_token(acc: np.ndarray, x_scale: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """y[m, n] = bf16(fp32(acc[m, n]) * fp32(s_x[m] * s_w[n])), bf16 bits [M, N]."""
+    sx = np.asarray(x_scale, dtype=np.float32).reshape(-1, 1)
+    comb = (sx * np.asarray(scales, dtype=np.float32).reshape(1, -1)).astype(np.float32)
+    accf = np.asarray(acc).astype(np.float32)
+    return f32_to_bf16_bits((accf * comb).astype(np.float32))
+
+
+def qlinear_w8a8_dynamic(xq: np.ndarray, x_scale: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+                         qtype: str, out: str = "bf16") -> np.ndarray:
+    """W8A8 GEMM on per-token quantized activations (row scales x_scale [M]).
+
+    out="acc" is the same accumulator as the static scheme's; out="bf16" applies
+    the per-token epilogue.
+    """
+    if out == "acc":
+        return qlinear_w8a8_static(xq, 1.0, codes, scales, qtype, out="acc")
+    return w8a8_epilogue_per_token(w8a8_accumulate(xq, codes, qtype), x_scale, scales)
 
 
 def reconstruction_error(w: np.ndarray, codes: np.ndarray, scales: np.ndarray, qtype: str):

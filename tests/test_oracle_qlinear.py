@@ -363,3 +363,101 @@ def test_w8a8_fp8_integer_weights_scale_one():
     acc = oracle.qlinear_w8a8_static(xq, 1.0, q, s, "fp8_e4m3fn", out="acc")
     ref = oracle.e4m3fn_decode(xq) @ W.astype(np.float64).T
     assert np.array_equal(acc.astype(np.float64), ref)
+
+
+# ---------------------------------------------------------------- dynamic per-token activations
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_act_dynamic_bruteforce(qtype):
+    # every row's scale and every code from exact rationals, row by row
+    _, _, x = synth.small_inputs(51, 5, 9, 1)
+    xf = oracle.bf16_bits_to_f32(x)
+    xf[2] = 0.0                                  # an all-zero row gets scale 1.0, codes 0
+    xb = oracle.f32_to_bf16_bits(xf)
+    q, s = oracle.quantize_act_dynamic(xb, qtype)
+    assert s.dtype == np.float32 and s.shape == (5,)
+    for m in range(5):
+        sm = _exact_scale(xf[m], qtype)
+        assert Fraction(float(s[m])) == sm
+        for k in range(9):
+            assert int(q[m, k]) & 0xFF == _exact_code(xf[m, k], sm, qtype) & 0xFF
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_act_dynamic_row_absmax_maps_to_qmax_and_rows_are_independent(qtype):
+    # rows of very different magnitude: a tensor-wide scale would crush the small rows
+    rng = np.random.default_rng(52)
+    xf = rng.standard_normal((4, 300)).astype(np.float32) * np.array([[1e-3], [1.0], [30.0], [1e3]], np.float32)
+    xb = oracle.f32_to_bf16_bits(xf)
+    q, s = oracle.quantize_act_dynamic(xb, qtype)
+    xr = oracle.bf16_bits_to_f32(xb)
+    for m in range(4):
+        i = np.abs(xr[m]).argmax()
+        top = 127 if qtype == "int8" else 448.0
+        val = float(q[m, i]) if qtype == "int8" else float(oracle.e4m3fn_decode(q[m, i:i + 1])[0])
+        assert abs(val) == top
+        q1, s1 = oracle.quantize_act_dynamic(xb[m:m + 1], qtype)     # the row alone
+        assert np.array_equal(q1[0], q[m]) and s1[0] == s[m]
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_act_dynamic_power_of_two_scaling(qtype):
+    # x -> 2^j x (exact in bf16) leaves the codes unchanged and scales s_x by 2^j
+    _, _, x = synth.small_inputs(53, 3, 64, 1)
+    xf = oracle.bf16_bits_to_f32(x)
+    q0, s0 = oracle.quantize_act_dynamic(x, qtype)
+    f = np.array([[2.0 ** -7], [1.0], [2.0 ** 9]], np.float32)
+    q1, s1 = oracle.quantize_act_dynamic(oracle.f32_to_bf16_bits(xf * f), qtype)
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(s1, (s0 * f[:, 0]).astype(np.float32))
+
+
+def test_act_dynamic_integer_rows_scale_one():
+    # integer rows whose absmax is 127 quantize to themselves at scale 1 (INT8)
+    rng = np.random.default_rng(54)
+    xf = rng.integers(-126, 127, size=(3, 40)).astype(np.float32)
+    xf[:, 5] = [127, -127, 127]
+    q, s = oracle.quantize_act_dynamic(oracle.f32_to_bf16_bits(xf), "int8")
+    assert np.all(s == 1.0) and np.array_equal(q.astype(np.float32), xf)
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_w8a8_dynamic_epilogue_bruteforce(qtype):
+    w, _, x = synth.small_inputs(55, 4, 8, 6)
+    gran = "per_channel" if qtype == "int8" else "per_tensor"
+    q, s = oracle.quantize_weight(w, qtype, gran)
+    xq, sx = oracle.quantize_act_dynamic(x, qtype)
+    y = oracle.qlinear_w8a8_dynamic(xq, sx, q, s, qtype)
+    for m in range(4):
+        for n in range(6):
+            acc = sum(_code_value(xq[m, k], qtype) * _code_value(q[n, k], qtype) for k in range(8))
+            comb = exact.f32(Fraction(float(sx[m])) * Fraction(float(s[n if s.size > 1 else 0])))
+            v = exact.bf16(exact.f32(exact.f32(acc) * comb))
+            assert y[m, n] == exact.bf16_bits_of(v)
+
+
+@pytest.mark.parametrize("qtype,gran", [("int8", "per_channel"), ("fp8_e4m3fn", "per_tensor")])
+def test_w8a8_dynamic_matches_bf16_dequant_reference(qtype, gran):
+    # same identity as the static scheme, with one scale per row of x
+    w, _, x = synth.small_inputs(56, 64, 1024, 256)
+    xf = oracle.bf16_bits_to_f32(x) * np.linspace(0.01, 50.0, 64, dtype=np.float32)[:, None]
+    x = oracle.f32_to_bf16_bits(xf)
+    q, s = oracle.quantize_weight(w, qtype, gran)
+    xq, sx = oracle.quantize_act_dynamic(x, qtype)
+    y = oracle.bf16_bits_to_f32(oracle.qlinear_w8a8_dynamic(xq, sx, q, s, qtype)).astype(np.float64)
+    dec = (lambda c: c.astype(np.float64)) if qtype == "int8" else oracle.e4m3fn_decode
+    xd = torch.from_numpy(dec(xq) * sx.astype(np.float64)[:, None]).to(torch.bfloat16)
+    wd = torch.from_numpy(dec(q) * s.astype(np.float64).reshape(-1, 1)).to(torch.bfloat16)
+    ref = (xd.float() @ wd.float().T).numpy().astype(np.float64)
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel < 4e-3
+    rms = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))      # per-row scale of y
+    assert np.max(np.abs(y - ref) / (np.abs(ref) + rms)) < 8e-3
+
+
+def test_w8a8_dynamic_accumulator_is_the_static_one():
+    w, _, x = synth.small_inputs(57, 7, 128, 9)
+    q, s = oracle.quantize_weight(w, "int8")
+    xq, sx = oracle.quantize_act_dynamic(x, "int8")
+    acc = oracle.qlinear_w8a8_dynamic(xq, sx, q, s, "int8", out="acc")
+    ref = xq.astype(np.int64) @ q.astype(np.int64).T            # numpy integer matmul
+    assert acc.dtype == np.int32 and np.array_equal(acc.astype(np.int64), ref)
