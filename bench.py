@@ -11,10 +11,16 @@ quantization"):
     * FP8 W8A8 static (per-tensor weight scale, per-layer input scales
       calibrated offline on a 64-row batch through the bf16-dequant chain),
   swept over M in {1, 16, 256, 1024}.
-One step = the 8 chains (2 variants x 4 M) = 864 GEMMs (+ 432 activation
-quantizations).  Each chain is captured once as a HIP graph and replayed, so
-the timed region holds GPU work only; weights (1.65 GiB per variant) are far
-larger than the 256 MB last-level cache, so every step streams them from HBM.
+One step = the 8 chains (2 variants x 4 M) = 864 GEMMs.  The FP8 W8A8 chain
+calls the fused static entry point (activation codes made inside the GEMM at
+M <= 16, one quantization pass before it above).  Each chain is captured once
+as a HIP graph and replayed, so the timed region holds GPU work only; weights
+(1.65 GiB per variant) are far larger than the 256 MB last-level cache, so
+every step streams them from HBM.
+
+`next_rows` (not part of the step or of `value`): the same stack in INT8 W8A8
+with dynamic per-token activation scales (quantize_act_dynamic +
+qlinear_w8a8_dynamic per layer), timed the same way after the main region.
 
 Output: one JSON line on stdout.  `value` is the whole step's TFLOP/s (2 M N K
 per GEMM); `cases` gives us, TFLOP/s, algorithmic GB/s and roofline fractions per
@@ -39,7 +45,8 @@ METRIC = "qlinear µs, TFLOP/s and HBM GB/s at M=1/16/256/1024; % of HBM/MFMA ro
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
 VARIANTS = (("int8_w8a16", "w8a16", "int8", "per_channel"),
-            ("fp8_w8a8_static", "w8a8_static", "fp8_e4m3fn", "per_tensor"))
+            ("fp8_w8a8_static", "w8a8_static_fused", "fp8_e4m3fn", "per_tensor"))
+NEXT_VARIANTS = (("int8_w8a8_dynamic", "w8a8_dynamic", "int8", "per_channel"),)
 
 
 def log(*a):
@@ -47,15 +54,22 @@ def log(*a):
 
 
 def gemm_bytes(scheme, M, K, N, per_tensor):
-    """Algorithmic HBM bytes of one GEMM call (codes + scales + activations in + out)."""
+    """Algorithmic HBM bytes of one layer call (weight codes + scales + activations in + out),
+    including the activation quantization the call implies:
+      w8a16               N K + scales + 2 M K + 2 M N
+      w8a8_static_fused   M <= 16: bf16 x read once by the GEMM: N K + scales + 2 M K + 2 M N
+                          M > 16: quantization pass (2 M K read, M K written) + GEMM on codes (M K)
+      w8a8_dynamic        quantization pass (2 M K read, M K + 4 M written) + GEMM (M K + 4 M)"""
     scale = 4 if per_tensor else 4 * N
     if scheme == "w8a16":
         return N * K + scale + 2 * M * K + 2 * M * N
+    if scheme == "w8a8_static_fused" and M <= 16:
+        return N * K + scale + 2 * M * K + 2 * M * N
+    if scheme == "w8a8_static_fused":
+        return N * K + scale + 4 * M * K + 2 * M * N
+    if scheme == "w8a8_dynamic":
+        return N * K + scale + 4 * M * K + 8 * M + 2 * M * N
     return N * K + scale + M * K + 2 * M * N
-
-
-def act_quant_bytes(M, K):
-    return 2 * M * K + M * K
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_gemm_mfma_int8_w8a16_stack.txt")
@@ -177,7 +191,7 @@ def main():
     torch.cuda.set_device(dev)
     L = args.layers
     qi, qf, sx = build_stack(qlq, synth, torch, dev, args.seed, L)
-    variants = {"int8_w8a16": qi, "fp8_w8a8_static": qf}
+    variants = {"int8_w8a16": qi, "fp8_w8a8_static": qf, "int8_w8a8_dynamic": qi}
 
     # buffers: inputs per M, ping-pong activations, codes, one shared workspace
     Ms = synth.STACK_M
@@ -188,15 +202,18 @@ def main():
         x0[M] = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     hbuf = [torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.bfloat16, device=dev) for _ in range(2)]
     xqbuf = torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.uint8, device=dev)
+    sxbuf = torch.empty(Mmax, dtype=torch.float32, device=dev)
     ws_need = 0
-    for _, scheme, qtype, _ in VARIANTS:
+    for _, scheme, qtype, _ in VARIANTS + NEXT_VARIANTS:
         for M in Ms:
             for _, K, N in synth.STACK_PROJS:
                 ws_need = max(ws_need, qlq.workspace_bytes(scheme, M, K, N, qtype))
     ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
 
+    scheme_of = {v[0]: v[1] for v in VARIANTS + NEXT_VARIANTS}
+
     def chain(vname, M):
-        scheme = "w8a16" if vname == "int8_w8a16" else "w8a8_static"
+        scheme = scheme_of[vname]
         h = x0[M]
         i = 0
         for l in range(L):
@@ -205,22 +222,25 @@ def main():
                 qw = variants[vname][l][p]
                 if scheme == "w8a16":
                     qlq.qlinear_w8a16(h, qw, out=out, workspace=ws)
+                elif scheme == "w8a8_static_fused":
+                    qlq.qlinear_w8a8_static_fused(h, sx[l][p], qw, out=out, workspace=ws)
                 else:
-                    xq = qlq.quantize_act_static(h, sx[l][p], "fp8_e4m3fn", out=xqbuf[: M * K].view(M, K))
-                    qlq.qlinear_w8a8_static(xq, sx[l][p], qw, out=out, workspace=ws)
+                    xq, xs = qlq.quantize_act_dynamic(h, "int8", out=xqbuf[: M * K].view(M, K), x_scale=sxbuf[:M])
+                    qlq.qlinear_w8a8_dynamic(xq, xs, qw, out=out, workspace=ws)
                 h = out
                 i += 1
         return h
 
     # capture one graph per (variant, M)
     cases = [(v[0], M) for v in VARIANTS for M in Ms]
+    next_cases = [(v[0], M) for v in NEXT_VARIANTS for M in Ms]
     graphs = {}
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
-    for c in cases:
+    for c in cases + next_cases:
         chain(*c)                                   # eager warm-up outside capture
     torch.cuda.synchronize()
-    for c in cases:
+    for c in cases + next_cases:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             chain(*c)
@@ -229,9 +249,9 @@ def main():
     log(f"[bench] captured {len(graphs)} graphs of {3 * L} GEMMs each")
 
     cur = torch.cuda.current_stream()
-    ev = {c: [] for c in cases}
+    ev = {c: [] for c in cases + next_cases}
 
-    def step(timed):
+    def step(timed, cases=cases):
         for c in cases:
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -252,34 +272,43 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    # the widened rows, timed after the main region (not part of the step)
+    for _ in range(args.warmup):
+        step(False, next_cases)
+    for _ in range(args.steps):
+        step(True, next_cases)
+    torch.cuda.synchronize()
 
     # per-case figures
-    out_cases = {}
-    tot_flops = 0
+    def figures(vlist, groups=None):
+        res, flops_all = {}, 0
+        for vname, scheme, qtype, gran in vlist:
+            for M in Ms:
+                us = sum(a.elapsed_time(b) for a, b in ev[(vname, M)]) * 1e3 / args.steps
+                flops = sum(2 * M * N * K for _, K, N in synth.STACK_PROJS) * L
+                byts = sum(gemm_bytes(scheme, M, K, N, gran == "per_tensor") for _, K, N in synth.STACK_PROJS) * L
+                dt = "bf16" if scheme == "w8a16" else ("fp8" if qtype == "fp8_e4m3fn" else "int8")
+                t_hbm = byts / (HBM_PEAK_GBS * 1e9) * 1e6
+                t_mfma = flops / (MFMA_PEAK_TFLOPS[dt] * 1e12) * 1e6
+                flops_all += flops
+                res[f"{vname}/M={M}"] = {
+                    "us_per_stack": round(us, 2), "us_per_gemm": round(us / (3 * L), 3),
+                    "tflops": round(flops / us / 1e6, 2), "gbs": round(byts / us / 1e3, 1),
+                    "hbm_frac": round(t_hbm / us, 3), "mfma_frac": round(t_mfma / us, 3),
+                    "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                    "frac": round(max(t_hbm, t_mfma) / us, 3)}
+                if groups is not None:
+                    fam = (vname, "small" if M <= 16 else "large")
+                    g = groups.setdefault(fam, {"us": 0.0, "flops": 0, "bytes": 0, "launches": 0, "dt": dt})
+                    g["us"] += us
+                    g["flops"] += flops
+                    g["bytes"] += byts
+                    g["launches"] += 3 * L
+        return res, flops_all
+
     groups = {}
-    for vname, scheme, qtype, gran in VARIANTS:
-        for M in Ms:
-            us = sum(a.elapsed_time(b) for a, b in ev[(vname, M)]) * 1e3 / args.steps
-            flops = sum(2 * M * N * K for _, K, N in synth.STACK_PROJS) * L
-            byts = sum(gemm_bytes(scheme, M, K, N, gran == "per_tensor") +
-                       (act_quant_bytes(M, K) if scheme == "w8a8_static" else 0)
-                       for _, K, N in synth.STACK_PROJS) * L
-            dt = "bf16" if scheme == "w8a16" else "fp8"
-            t_hbm = byts / (HBM_PEAK_GBS * 1e9) * 1e6
-            t_mfma = flops / (MFMA_PEAK_TFLOPS[dt] * 1e12) * 1e6
-            tot_flops += flops
-            out_cases[f"{vname}/M={M}"] = {
-                "us_per_stack": round(us, 2), "us_per_gemm": round(us / (3 * L), 3),
-                "tflops": round(flops / us / 1e6, 2), "gbs": round(byts / us / 1e3, 1),
-                "hbm_frac": round(t_hbm / us, 3), "mfma_frac": round(t_mfma / us, 3),
-                "bound": "hbm" if t_hbm >= t_mfma else "mfma",
-                "frac": round(max(t_hbm, t_mfma) / us, 3)}
-            fam = (vname, "small" if M <= 16 else "large")
-            g = groups.setdefault(fam, {"us": 0.0, "flops": 0, "bytes": 0, "launches": 0, "dt": dt})
-            g["us"] += us
-            g["flops"] += flops
-            g["bytes"] += byts
-            g["launches"] += 3 * L
+    out_cases, tot_flops = figures(VARIANTS, groups)
+    next_cases_out, _ = figures(NEXT_VARIANTS)
     # dominant kernel: the (variant, kernel family) group with the most time
     fam, g = max(groups.items(), key=lambda kv: kv[1]["us"])
     avg_us = g["us"] / g["launches"]
@@ -298,7 +327,7 @@ def main():
     kernel_name = {("int8_w8a16", "large"): "gemm_mfma_kernel<int8, W8A16, *> (M=256 and M=1024 launches)",
                    ("int8_w8a16", "small"): "gemm_small_kernel<int8, W8A16> (M=1 and M=16 launches)",
                    ("fp8_w8a8_static", "large"): "gemm_mfma_kernel<fp8, W8A8, *> + quant_act_kernel<fp8>",
-                   ("fp8_w8a8_static", "small"): "gemm_small_kernel<fp8, W8A8> + quant_act_kernel<fp8>"}[fam]
+                   ("fp8_w8a8_static", "small"): "gemm_small_kernel<fp8, W8A8, fused quantization>"}[fam]
     roof["kernel"] = kernel_name
     roof["avg_launch_us"] = round(avg_us, 3)
     roof["launches_per_step"] = g["launches"]
@@ -312,7 +341,10 @@ def main():
                                    f"static; M in {{1,16,256,1024}}; one HIP graph per chain",
                        "layers": L, "M": list(Ms), "variants": [v[0] for v in VARIANTS],
                        "gemms_per_step": 3 * L * len(cases)},
-            "cases": out_cases, "roofline": roof}
+            "cases": out_cases, "roofline": roof,
+            "next_rows": {"note": "INT8 W8A8 with dynamic per-token activation scales on the same stack; "
+                                  "timed after the step, not part of value or ms_per_step",
+                          "cases": next_cases_out}}
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -71,8 +71,10 @@ typedef enum {
 
 /* Which GEMM a workspace is sized for. */
 typedef enum {
-  QLQ_SCHEME_W8A16 = 0,
-  QLQ_SCHEME_W8A8_STATIC = 1
+  QLQ_SCHEME_W8A16 = 0,               /* qlq_qlinear_w8a16 */
+  QLQ_SCHEME_W8A8_STATIC = 1,         /* qlq_qlinear_w8a8_static */
+  QLQ_SCHEME_W8A8_STATIC_FUSED = 2,   /* qlq_qlinear_w8a8_static_fused */
+  QLQ_SCHEME_W8A8_DYNAMIC = 3         /* qlq_qlinear_w8a8_dynamic */
 } qlq_scheme;
 
 /* ------------------------------------------------------------------ sizing */
@@ -129,6 +131,16 @@ qlq_status qlq_calibrate_input_scale(const void* x_calib_bf16, int64_t numel, ql
 qlq_status qlq_quantize_act_static(const void* x_bf16, int64_t M, int64_t K, float input_scale,
                                    qlq_qtype qtype, void* xq, hipStream_t stream);
 
+/* Dynamic per-token activation quantization, the run-time alternative that the
+ * key-design list of the INT8 section contrasts with static scaling (one more
+ * reduction per call).  For every row m, with qmax = 127 (INT8) or 448 (e4m3fn):
+ *   x_scale[m] = absmax_k |x[m,k]| / qmax   (fp32 division; 1 for an all-zero row)
+ *   xq[m,k]    = sat(round-to-nearest-even(x[m,k] / x_scale[m]))   (fp32 division)
+ * i.e. the weight quantizer's per-channel rule applied to each row of x.
+ * x bf16 [M, K]; xq [M, K] one byte per code; x_scale fp32 [M] (device). */
+qlq_status qlq_quantize_act_dynamic(const void* x_bf16, int64_t M, int64_t K, qlq_qtype qtype,
+                                    void* xq, float* x_scale, hipStream_t stream);
+
 /* -------------------------------------------------------------------- GEMMs */
 
 /* Weight-only quantized linear (W8A16):
@@ -152,6 +164,35 @@ qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale,
                                    int64_t w_scale_numel, qlq_qtype qtype, qlq_out out,
                                    void* y, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* W8A8 static from bf16 activations: the same result as qlq_quantize_act_static
+ * followed by qlq_qlinear_w8a8_static (identical codes, accumulators and
+ * outputs), as one call.  The codes go through the workspace: one quantization
+ * pass writes them, the GEMM reads them.  (Quantizing inside the GEMM kernels
+ * measured slower on MI355X: the small-M kernel would divide every x element
+ * once per 16-column tile, and bf16 x tiles would double the bytes each CU
+ * streams through the large-M main loop.)  Size the workspace with
+ * qlq_workspace_bytes(QLQ_SCHEME_W8A8_STATIC_FUSED, ...); it follows the same
+ * zero-fill rule as every other workspace. */
+qlq_status qlq_qlinear_w8a8_static_fused(const void* x_bf16, float input_scale,
+                                         int64_t M, int64_t K, int64_t N,
+                                         const void* wq_packed, const float* w_scale,
+                                         int64_t w_scale_numel, qlq_qtype qtype, qlq_out out,
+                                         void* y, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* W8A8 with per-token activation scales (codes and scales from
+ * qlq_quantize_act_dynamic):
+ *   acc[m,n] = sum_k xq[m,k] * q[n,k]   (as in qlq_qlinear_w8a8_static)
+ *   y[m,n]   = bf16( fp32(acc[m,n]) * fp32(x_scale[m] * s[n]) )
+ * x_scale fp32 [M] (device).  out, workspace and the INT8 K bound as for the
+ * static call; size the workspace with QLQ_SCHEME_W8A8_DYNAMIC. */
+qlq_status qlq_qlinear_w8a8_dynamic(const void* xq, const float* x_scale,
+                                    int64_t M, int64_t K, int64_t N,
+                                    const void* wq_packed, const float* w_scale,
+                                    int64_t w_scale_numel, qlq_qtype qtype, qlq_out out,
+                                    void* y, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------- errors */
 

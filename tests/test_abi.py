@@ -114,3 +114,49 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         qlq.quantize_weight(torch.zeros(4, 4), "int8")
+
+
+def test_header_declares_the_next_rows():
+    names = _declared()
+    for n in ["qlq_quantize_act_dynamic", "qlq_qlinear_w8a8_dynamic", "qlq_qlinear_w8a8_static_fused"]:
+        assert n in names
+
+
+def test_fused_and_dynamic_workspace_sizes():
+    for M, K, N in [(1, 2048, 2048), (16, 2048, 11008), (1, 11008, 2048), (17, 64, 16), (256, 11008, 2048),
+                    (1024, 2048, 11008)]:
+        for qtype in ["int8", "fp8_e4m3fn"]:
+            g = qlq.workspace_bytes("w8a8_static", M, K, N, qtype)
+            assert qlq.workspace_bytes("w8a8_dynamic", M, K, N, qtype) == g
+            # the codes live after the GEMM's region and never below the 4 KiB counter region
+            f = qlq.workspace_bytes("w8a8_static_fused", M, K, N, qtype)
+            assert f >= max(g, 4096) + M * K and f - M * K >= 4096 and (f - M * K) % 256 == 0
+
+
+def test_validation_of_the_next_rows():
+    L = qlq.lib()
+    st, msg = _status(L.qlq_quantize_act_dynamic, FAKE, 4, 64, 0, FAKE, None, None)
+    assert st == 1 and "null" in msg
+    st, _ = _status(L.qlq_quantize_act_dynamic, FAKE, 0, 64, 0, FAKE, FAKE, None)
+    assert st == 1
+    st, _ = _status(L.qlq_quantize_act_dynamic, FAKE, 4, 64, 3, FAKE, FAKE, None)
+    assert st == 2
+    st, msg = _status(L.qlq_qlinear_w8a8_dynamic, FAKE, None, 4, 64, 16, FAKE, FAKE, 16, 0, 0, FAKE, None, 0, None)
+    assert st == 1 and "null" in msg
+    st, msg = _status(L.qlq_qlinear_w8a8_dynamic, FAKE, FAKE, 4, 133145, 16, FAKE, FAKE, 16, 0, 0, FAKE, None, 0,
+                      None)
+    assert st == 1 and "133144" in msg
+    st, _ = _status(L.qlq_qlinear_w8a8_dynamic, FAKE, FAKE, 4, 64, 16, FAKE, FAKE, 16, 0, 5, FAKE, None, 0, None)
+    assert st == 2
+    for bad in [0.0, -2.0, float("nan")]:
+        st, msg = _status(L.qlq_qlinear_w8a8_static_fused, FAKE, bad, 4, 64, 16, FAKE, FAKE, 16, 0, 0, FAKE, None,
+                          0, None)
+        assert st == 1 and "input_scale" in msg
+    # the fused call keeps its codes in the workspace
+    need = qlq.workspace_bytes("w8a8_static_fused", 64, 128, 32, "int8")
+    st, msg = _status(L.qlq_qlinear_w8a8_static_fused, FAKE, 1.0, 64, 128, 32, FAKE, FAKE, 32, 0, 0, FAKE, FAKE,
+                      need - 1, None)
+    assert st == 1 and "workspace" in msg
+    st, msg = _status(L.qlq_qlinear_w8a8_static_fused, FAKE, 1.0, 64, 128, 32, FAKE, FAKE, 32, 0, 0, FAKE,
+                      ctypes.c_void_p(0x10010), need, None)
+    assert st == 1 and "256-byte" in msg

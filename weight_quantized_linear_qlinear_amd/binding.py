@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlq.so"
 QTYPES = {"int8": 0, "fp8_e4m3fn": 1}
 GRANULARITIES = {"per_channel": 0, "per_tensor": 1}
 OUTS = {"bf16": 0, "acc": 1}
-SCHEMES = {"w8a16": 0, "w8a8_static": 1}
+SCHEMES = {"w8a16": 0, "w8a8_static": 1, "w8a8_static_fused": 2, "w8a8_dynamic": 3}
 STATUS = {0: "QLQ_OK", 1: "QLQ_ERR_INVALID_ARG", 2: "QLQ_ERR_UNSUPPORTED", 3: "QLQ_ERR_HIP"}
 
 # name -> (restype, argtypes), mirroring include/qlq.h
@@ -39,6 +39,14 @@ _SIGNATURES = {
     "qlq_qlinear_w8a8_static": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
                                            _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
                                            _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_quantize_act_dynamic": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
+                                            _c.c_void_p, _c.c_void_p]),
+    "qlq_qlinear_w8a8_static_fused": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                 _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
+                                                 _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_qlinear_w8a8_dynamic": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                                            _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
+                                            _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "qlq_status_string": (_c.c_char_p, [_c.c_int]),
     "qlq_last_error": (_c.c_char_p, []),
     "qlq_version": (_c.c_char_p, []),
@@ -198,6 +206,22 @@ def quantize_act_static(x: torch.Tensor, input_scale: float, qtype: str,
     return out
 
 
+def quantize_act_dynamic(x: torch.Tensor, qtype: str, out: torch.Tensor | None = None,
+                         x_scale: torch.Tensor | None = None):
+    """Per-token codes of x [M, K] bf16 and their row scales: (xq [M, K], x_scale fp32 [M])."""
+    _require_gpu(x)
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=code_dtype(qtype), device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().qlq_quantize_act_dynamic(_ptr(x), M, K, _qtype(qtype), _ptr(out), _ptr(x_scale),
+                                          _stream(x.device)))
+    return out, x_scale
+
+
 # ---------------------------------------------------------------------- GEMMs
 def qlinear_w8a16(x: torch.Tensor, qw: QuantizedWeight, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -235,4 +259,50 @@ def qlinear_w8a8_static(xq: torch.Tensor, input_scale: float, qw: QuantizedWeigh
                                          _ptr(qw.scale), qw.scale.numel(), _qtype(qw.qtype), OUTS[out_mode],
                                          _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
                                          _stream(xq.device)))
+    return out
+
+
+def _w8a8_out(M: int, qw: QuantizedWeight, out_mode: str, dev: torch.device) -> torch.Tensor:
+    if out_mode == "acc":
+        dt = torch.int32 if qw.qtype == "int8" else torch.float32
+    else:
+        dt = torch.bfloat16
+    return torch.empty((M, qw.N), dtype=dt, device=dev)
+
+
+def qlinear_w8a8_static_fused(x: torch.Tensor, input_scale: float, qw: QuantizedWeight, out_mode: str = "bf16",
+                              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """quantize_act_static + qlinear_w8a8_static in one call, from bf16 x [M, K]."""
+    _require_gpu(x)
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.shape[1] != qw.K:
+        raise ValueError(f"x must be bf16 [M, {qw.K}]")
+    M = x.shape[0]
+    if out is None:
+        out = _w8a8_out(M, qw, out_mode, x.device)
+    nbytes = workspace_bytes("w8a8_static_fused", M, qw.K, qw.N, qw.qtype)
+    ws = workspace if workspace is not None else _workspace(x.device, nbytes)
+    _check(lib().qlq_qlinear_w8a8_static_fused(_ptr(x), float(input_scale), M, qw.K, qw.N, _ptr(qw.packed),
+                                               _ptr(qw.scale), qw.scale.numel(), _qtype(qw.qtype), OUTS[out_mode],
+                                               _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                               _stream(x.device)))
+    return out
+
+
+def qlinear_w8a8_dynamic(xq: torch.Tensor, x_scale: torch.Tensor, qw: QuantizedWeight, out_mode: str = "bf16",
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W8A8 GEMM on per-token codes xq [M, K] with row scales x_scale fp32 [M]."""
+    _require_gpu(xq, x_scale)
+    if xq.dim() != 2 or xq.element_size() != 1 or xq.shape[1] != qw.K:
+        raise ValueError(f"xq must be 1-byte codes [M, {qw.K}]")
+    M = xq.shape[0]
+    if x_scale.dtype != torch.float32 or x_scale.numel() != M:
+        raise ValueError(f"x_scale must be fp32 [{M}]")
+    if out is None:
+        out = _w8a8_out(M, qw, out_mode, xq.device)
+    nbytes = workspace_bytes("w8a8_dynamic", M, qw.K, qw.N, qw.qtype)
+    ws = workspace if workspace is not None else _workspace(xq.device, nbytes)
+    _check(lib().qlq_qlinear_w8a8_dynamic(_ptr(xq), _ptr(x_scale), M, qw.K, qw.N, _ptr(qw.packed),
+                                          _ptr(qw.scale), qw.scale.numel(), _qtype(qw.qtype), OUTS[out_mode],
+                                          _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                          _stream(xq.device)))
     return out

@@ -208,13 +208,31 @@ size_t qlq_packed_weight_bytes(int64_t N, int64_t K) {
   return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K, 64) * 64;
 }
 
+// Workspace of the GEMM proper (split-K counters and partials).  The call picks
+// the direct-to-LDS kernel only for aligned x, so this covers both plans.
+static size_t gemm_ws_bytes(int scheme, int64_t M, int64_t K, int64_t N, int qtype) {
+  const size_t a = qlq::plan_gemm(scheme, qtype, M, K, N, true).ws_bytes;
+  const size_t b = qlq::plan_gemm(scheme, qtype, M, K, N, false).ws_bytes;
+  return a > b ? a : b;
+}
+
+// Fused static W8A8: offset of the activation codes inside the workspace.  They go after the GEMM's region and never below the counter
+// region, so the counters (which every call leaves at zero) are never
+// overwritten by codes, whatever M earlier calls on the same buffer used.
+static size_t fused_xq_offset(int64_t M, int64_t K, int64_t N, int qtype) {
+  const size_t g = (gemm_ws_bytes(qlq::kW8A8, M, K, N, qtype) + 255) / 256 * 256;
+  return g > kCounterBytes ? g : kCounterBytes;
+}
+
 size_t qlq_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype) {
   if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
-  if (scheme != QLQ_SCHEME_W8A16 && scheme != QLQ_SCHEME_W8A8_STATIC) return 0;
-  // The call picks the direct-to-LDS kernel only for aligned x; size for both.
-  const size_t a = qlq::plan_gemm((int)scheme, (int)qtype, M, K, N, true).ws_bytes;
-  const size_t b = qlq::plan_gemm((int)scheme, (int)qtype, M, K, N, false).ws_bytes;
-  return a > b ? a : b;
+  switch (scheme) {
+    case QLQ_SCHEME_W8A16: return gemm_ws_bytes(qlq::kW8A16, M, K, N, (int)qtype);
+    case QLQ_SCHEME_W8A8_STATIC:
+    case QLQ_SCHEME_W8A8_DYNAMIC: return gemm_ws_bytes(qlq::kW8A8, M, K, N, (int)qtype);
+    case QLQ_SCHEME_W8A8_STATIC_FUSED: return fused_xq_offset(M, K, N, (int)qtype) + (size_t)M * (size_t)K;
+  }
+  return 0;
 }
 
 qlq_status qlq_quantize_weight(const void* w, int w_is_bf16, int64_t N, int64_t K, qlq_qtype qtype,
@@ -263,9 +281,21 @@ qlq_status qlq_quantize_act_static(const void* x_bf16, int64_t M, int64_t K, flo
                     "quantize_act_static");
 }
 
+qlq_status qlq_quantize_act_dynamic(const void* x_bf16, int64_t M, int64_t K, qlq_qtype qtype, void* xq,
+                                    float* x_scale, hipStream_t stream) {
+  if (!x_bf16 || !xq || !x_scale) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(M, K, 1)) return st;
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (!aligned(x_bf16, 2) || !aligned(x_scale, 4)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(qlq::launch_quant_act_dynamic(x_bf16, (int)M, (int)K, (int)qtype, xq, x_scale, stream),
+                    "quantize_act_dynamic");
+}
+
+// x: bf16 for W8A16, codes for W8A8.
 static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int64_t N, const void* wq_packed,
                            const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
-                           int out_acc, void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                           const float* row_scale, int out_acc, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, const char* what) {
   if (!x || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
   if (qlq_status st = check_dims(M, K, N)) return st;
   if (qlq_status st = check_qtype(qtype)) return st;
@@ -273,7 +303,8 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
     return fail(QLQ_ERR_INVALID_ARG, "w_scale_numel must be 1 or N (got %lld, N=%lld)", (long long)w_scale_numel,
                 (long long)N);
   if (!aligned(wq_packed, 16)) return fail(QLQ_ERR_INVALID_ARG, "wq_packed must be 16-byte aligned");
-  if (!aligned(w_scale, 4) || !aligned(y, 4) || !aligned(x, scheme == qlq::kW8A16 ? 2 : 1))
+  if (!aligned(w_scale, 4) || !aligned(y, 4) || !aligned(x, scheme == qlq::kW8A16 ? 2 : 1) ||
+      !aligned(row_scale, 4))
     return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
   const bool fast = (K % 64 == 0) && aligned(x, 16);
   qlq::GemmPlan plan = qlq::plan_gemm(scheme, (int)qtype, M, K, N, fast);
@@ -301,19 +332,20 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.KT = (int)cdiv(K, 64);
   a.NT = (int)cdiv(N, 16);
   a.input_scale = input_scale;
+  a.row_scale = row_scale;
   a.out_acc = out_acc;
   a.fast = fast;
   hipError_t e = plan.kind == 0   ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
                  : plan.kind == 1 ? qlq::launch_gemm_large(scheme, (int)qtype, plan, a, stream)
                                   : qlq::launch_gemm_mfma(scheme, (int)qtype, plan, a, stream);
-  return hip_status(e, scheme == qlq::kW8A16 ? "qlinear_w8a16" : "qlinear_w8a8_static");
+  return hip_status(e, what);
 }
 
 qlq_status qlq_qlinear_w8a16(const void* x_bf16, int64_t M, int64_t K, int64_t N, const void* wq_packed,
                              const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, void* y_bf16,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return run_gemm(qlq::kW8A16, x_bf16, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, 1.0f, 0, y_bf16,
-                  workspace, workspace_bytes, stream);
+  return run_gemm(qlq::kW8A16, x_bf16, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, 1.0f, nullptr, 0,
+                  y_bf16, workspace, workspace_bytes, stream, "qlinear_w8a16");
 }
 
 qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale, int64_t M, int64_t K, int64_t N,
@@ -325,8 +357,52 @@ qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale, int64_t M,
   if (qtype == QLQ_INT8 && K > kMaxInt8K)
     return fail(QLQ_ERR_INVALID_ARG, "INT8 W8A8 needs K <= %lld for an exact int32 accumulator",
                 (long long)kMaxInt8K);
-  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale,
-                  out == QLQ_OUT_ACC ? 1 : 0, y, workspace, workspace_bytes, stream);
+  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale, nullptr,
+                  out == QLQ_OUT_ACC ? 1 : 0, y, workspace, workspace_bytes, stream, "qlinear_w8a8_static");
+}
+
+static qlq_status check_w8a8(qlq_qtype qtype, qlq_out out, int64_t K) {
+  if (out != QLQ_OUT_BF16 && out != QLQ_OUT_ACC) return fail(QLQ_ERR_UNSUPPORTED, "unknown out mode %d", (int)out);
+  if (qtype == QLQ_INT8 && K > kMaxInt8K)
+    return fail(QLQ_ERR_INVALID_ARG, "INT8 W8A8 needs K <= %lld for an exact int32 accumulator",
+                (long long)kMaxInt8K);
+  return QLQ_OK;
+}
+
+qlq_status qlq_qlinear_w8a8_static_fused(const void* x_bf16, float input_scale, int64_t M, int64_t K, int64_t N,
+                                         const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                                         qlq_qtype qtype, qlq_out out, void* y, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  if (qlq_status st = check_scale(input_scale, "input_scale")) return st;
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (qlq_status st = check_w8a8(qtype, out, K)) return st;
+  // one quantization pass into the workspace, then the GEMM on the codes
+  if (!x_bf16 || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(M, K, N)) return st;
+  if (!aligned(x_bf16, 2)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  const size_t off = fused_xq_offset(M, K, N, (int)qtype);
+  const size_t need = off + (size_t)M * (size_t)K;
+  if (!workspace || workspace_bytes < need)
+    return fail(QLQ_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  void* xq = static_cast<uint8_t*>(workspace) + off;
+  if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream),
+                                 "qlinear_w8a8_static_fused"))
+    return st;
+  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale, nullptr,
+                  out == QLQ_OUT_ACC ? 1 : 0, y, workspace, off, stream, "qlinear_w8a8_static_fused");
+}
+
+qlq_status qlq_qlinear_w8a8_dynamic(const void* xq, const float* x_scale, int64_t M, int64_t K, int64_t N,
+                                    const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                                    qlq_qtype qtype, qlq_out out, void* y, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!x_scale) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (qlq_status st = check_w8a8(qtype, out, K)) return st;
+  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, 1.0f, x_scale,
+                  out == QLQ_OUT_ACC ? 1 : 0, y, workspace, workspace_bytes, stream, "qlinear_w8a8_dynamic");
 }
 
 }  // extern "C"

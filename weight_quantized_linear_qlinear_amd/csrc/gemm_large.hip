@@ -286,8 +286,8 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
   for (int j = 0; j < TN; ++j) {
     const int n = (nt0 + wn * TN + j) * kTileN + r;
     if (n >= a.N) continue;
-    float comb = 0.0f;
-    if (SCH == kW8A8 && !a.out_acc) comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
+    float sw = 0.0f;
+    if (SCH == kW8A8 && !a.out_acc) sw = a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -301,7 +301,8 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
           if constexpr (T::kIntAcc) reinterpret_cast<int32_t*>(a.y)[o] = acci[i][j][jj];
           else reinterpret_cast<float*>(a.y)[o] = accf[i][j][jj];
         } else {
-          float v = T::kIntAcc ? (float)acci[i][j][jj] : accf[i][j][jj];
+          const float v = T::kIntAcc ? (float)acci[i][j][jj] : accf[i][j][jj];
+          const float comb = (a.row_scale ? a.row_scale[m] : a.input_scale) * sw;   // fp32(s_x * s_w[n])
           reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
         }
       }

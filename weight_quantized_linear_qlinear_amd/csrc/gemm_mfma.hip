@@ -186,8 +186,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     sc_m128[j] = -128.0f * v;
   }
 
-  // W8A8 per-tensor combined scale s_x * s_w, loaded before the main loop
-  const float comb_t = (SCH == kW8A8 && a.scale_per_tensor) ? a.input_scale * a.w_scale[0] : 1.0f;
+  // W8A8 per-tensor weight scale, loaded before the main loop
+  const float sw_t = (SCH == kW8A8 && a.scale_per_tensor) ? a.w_scale[0] : 1.0f;
 
   f32x16 accf[TM][TN];
   i32x16 acci[TM][TN];
@@ -375,22 +375,31 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     constexpr int PITCH = BN * 2 + 16;                       // bytes per staged row (padding spreads banks)
     static_assert(BM * PITCH <= kLdsBytes<QT, SCH, BM, BN, BKT, NSTAGE>(), "staging fits the LDS allocation");
     __syncthreads();                                         // every wave is done with the stage buffers
-    // W8A8 combined scales s_x * s_w[n] for this lane's 4 TN groups of four columns
-    // (all loads issued before the first use; N % 8 == 0 here, so n < N implies n + 3 < N)
-    f32x4 comb[TN][4];
+    // W8A8 scales for this lane's TN x 4 groups of four columns and TM rows: the
+    // element scale is fp32(s_x * s_w[n]), s_x the static input scale or the
+    // row's per-token scale.  All loads are issued before the first use
+    // (N % 8 == 0 here, so n < N implies n + 3 < N).
+    f32x4 sw[TN][4];
+    float rf[TM];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        comb[j][g] = (f32x4){comb_t, comb_t, comb_t, comb_t};
+        sw[j][g] = (f32x4){sw_t, sw_t, sw_t, sw_t};
         if (SCH == kW8A8 && !a.scale_per_tensor) {
           const int n = nt0 * 16 + (wn * TN + j) * 32 + 8 * g + 4 * kg;
           if (n < a.N) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) comb[j][g][c] = a.input_scale * a.w_scale[n + c];
+            for (int c = 0; c < 4; ++c) sw[j][g][c] = a.w_scale[n + c];
           }
         }
       }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + (wm * TM + i) * 32 + l32;
+      rf[i] = a.input_scale;
+      if (SCH == kW8A8 && a.row_scale) rf[i] = m < a.M ? a.row_scale[m] : 0.0f;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -402,7 +411,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             if constexpr (SCH == kW8A16) v[c] = accf[i][j][4 * g + c];
-            else v[c] = (T::kIntAcc ? (float)acci[i][j][4 * g + c] : accf[i][j][4 * g + c]) * comb[j][g][c];
+            else v[c] = (T::kIntAcc ? (float)acci[i][j][4 * g + c] : accf[i][j][4 * g + c]) * (rf[i] * sw[j][g][c]);
           }
           const int row = (wm * TM + i) * 32 + l32;
           *reinterpret_cast<u32x2*>(smem + row * PITCH + col * 2) = pack_bf16x4(v);
@@ -445,7 +454,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
             if constexpr (T::kIntAcc) reinterpret_cast<int32_t*>(a.y)[o] = acci[i][j][e];
             else reinterpret_cast<float*>(a.y)[o] = accf[i][j][e];
           } else {
-            const float comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
+            const float sx = a.row_scale ? a.row_scale[m] : a.input_scale;
+            const float comb = sx * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
             const float v = T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e];
             reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
           }

@@ -9,6 +9,7 @@
 //   W8A16: codes -> bf16(fp32(q) * s[n]) in registers -> v_mfma_f32_16x16x32_bf16
 //   W8A8 INT8: v_mfma_i32_16x16x64_i8 on the codes (exact int32)
 //   W8A8 FP8:  v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3) on the codes
+// The W8A8 epilogue takes a per-token scale per row when the call passes one.
 // M <= 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
 //
 // Work split: workgroup (nt, s) owns output columns [16 nt, 16 nt + 16) and the
@@ -74,6 +75,7 @@ template <int QT, int SCH, bool FAST>
 __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int ups, int upw) {
   using T = SmallTraits<QT, SCH>;
   constexpr int TPU = T::kTilesPerUnit;
+  constexpr int kU = kUnroll;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = blockIdx.x % a.NT;
   const int s = blockIdx.x / a.NT;
@@ -98,12 +100,12 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
 
   // All loads of the wave's K slice (at most kUnroll units, see plan_gemm) are
   // issued before the first wait: one memory round trip per wave.
-  for (int u0 = u_begin; u0 < u_end; u0 += kUnroll) {
-    u32x4 wv[kUnroll][TPU];
-    u32x4 xa[kUnroll][TPU];      // A operand bytes: 16 codes, or 8 bf16 (W8A16 uses 2 regs per unit)
-    u32x4 xb[kUnroll];           // W8A16: bf16 k + 8 .. k + 15
+  for (int u0 = u_begin; u0 < u_end; u0 += kU) {
+    u32x4 wv[kU][TPU];
+    u32x4 xa[kU][TPU];      // A operand bytes: 16 codes, or 8 bf16 (W8A16: values 0..7)
+    u32x4 xb[kU][TPU];      // W8A16: bf16 values 8 .. 15
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < kU; ++i) {
       const bool live = u0 + i < u_end;
 #pragma unroll
       for (int t = 0; t < TPU; ++t) {
@@ -111,11 +113,11 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
         const bool ok = live && kt < a.KT;
         wv[i][t] = ok ? ld16_stream(wbase + (int64_t)kt * kTileBytes) : (u32x4){0u, 0u, 0u, 0u};
         xa[i][t] = (u32x4){0u, 0u, 0u, 0u};
+        xb[i][t] = (u32x4){0u, 0u, 0u, 0u};
         if constexpr (SCH == kW8A16) {
-          xb[i] = (u32x4){0u, 0u, 0u, 0u};
           if (ok && row_ok)
             load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, kt * kTileK + g * 16,
-                                 a.K, xa[i][t], xb[i]);
+                                 a.K, xa[i][t], xb[i][t]);
         } else {
           if (ok && row_ok)
             xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K,
@@ -124,13 +126,13 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
       }
     }
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < kU; ++i) {
       if (u0 + i >= u_end) break;
       if constexpr (SCH == kW8A16) {
         bf16x8 b0 = dequant8<QT>(wv[i][0].x, wv[i][0].y, sc, sc_m128);
         bf16x8 b1 = dequant8<QT>(wv[i][0].z, wv[i][0].w, sc, sc_m128);
         accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[i][0]), b0, accf);
-        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[i]), b1, accf);
+        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[i][0]), b1, accf);
       } else if constexpr (QT == kInt8) {
         acci = mfma_i8_k64(xa[i][0], wv[i][0], acci);
       } else {
@@ -180,9 +182,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
 
   // ---- epilogue: lane holds D[4g + j][r] = y[m = 4g + j, n]
   if (n >= a.N) return;
-  float comb = 0.0f;
-  if (SCH == kW8A8 && !a.out_acc)
-    comb = a.input_scale * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
+  float sw = 0.0f;
+  if (SCH == kW8A8 && !a.out_acc) sw = a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = 4 * g + j;
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
     } else if (a.out_acc) {
       reinterpret_cast<float*>(a.y)[o] = tot[j];   // int32 bits or fp32
     } else {
-      float v = T::kIntAcc ? (float)__builtin_bit_cast(i32x4, tot)[j] : tot[j];
+      const float v = T::kIntAcc ? (float)__builtin_bit_cast(i32x4, tot)[j] : tot[j];
+      const float comb = (a.row_scale ? a.row_scale[m] : a.input_scale) * sw;   // fp32(s_x * s_w[n])
       reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
     }
   }

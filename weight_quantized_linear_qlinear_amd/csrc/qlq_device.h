@@ -70,6 +70,16 @@ __device__ __forceinline__ uint32_t f32_to_i8_sat(float v) {
   return (uint32_t)((int)r) & 0xFFu;
 }
 
+// Activation codes: four bf16 (two dwords) -> four codes of sat(RNE(x / s)), an
+// IEEE fp32 division per value (callers must not build with fast-math).
+template <int QT>
+__device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s) {
+  float a = bf16_bits_to_f32(lo & 0xFFFF) / s, b = bf16_bits_to_f32(lo >> 16) / s;
+  float c = bf16_bits_to_f32(hi & 0xFFFF) / s, d = bf16_bits_to_f32(hi >> 16) / s;
+  if constexpr (QT == kFp8) return f32x4_to_e4m3x4_sat(a, b, c, d);
+  return f32_to_i8_sat(a) | (f32_to_i8_sat(b) << 8) | (f32_to_i8_sat(c) << 16) | (f32_to_i8_sat(d) << 24);
+}
+
 // Dequantize 8 codes (two dwords) to 8 bf16 = bf16(fp32(q) * s), one fp32
 // rounding for the product and one for the bf16 cast.
 template <int QT>

@@ -40,6 +40,7 @@ struct GemmArgs {
   uint32_t partials_bytes;  // size of the partial region
   int M, K, N, KT, NT;
   float input_scale;
+  const float* row_scale;   // W8A8 per-token activation scales [M], or null (static input_scale)
   int out_acc;
   int fast;                 // K % 64 == 0 and 16-byte aligned rows/pointers
 };
@@ -62,6 +63,8 @@ hipError_t launch_pack_weight(const void* w, int is_bf16, int N, int K, int qtyp
                               uint8_t* packed, float* w_scale, hipStream_t st);
 hipError_t launch_unpack_weight(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st);
 hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st);
+hipError_t launch_quant_act_dynamic(const void* x, int M, int K, int qtype, void* xq, float* x_scale,
+                                   hipStream_t st);
 
 // Raises kernel k's dynamic-LDS limit to `bytes` on the current device, once per
 // device (bit d of `done` records device d; devices past 63 set it every call).

@@ -1,5 +1,5 @@
 // Quantizers: weight absmax / scale / codes / packing, static activation
-// calibration and static activation quantization.
+// calibration, static and dynamic (per-token) activation quantization.
 //
 // What they compute (symmetric, no zero point; "Nano-vLLM-MOE" README mirror,
 // section "INT8 量化支持", scheme table and key-design list; "Nano-vLLM-MoE"
@@ -122,14 +122,6 @@ __global__ __launch_bounds__(256) void unpack_weight_kernel(const uint8_t* packe
 // Eight bf16 -> eight codes per thread on the vector path (16-byte load, 8-byte
 // store); element by element for the tail or unaligned buffers.
 template <int QT>
-__device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s) {
-  float a = bf16_bits_to_f32(lo & 0xFFFF) / s, b = bf16_bits_to_f32(lo >> 16) / s;
-  float c = bf16_bits_to_f32(hi & 0xFFFF) / s, d = bf16_bits_to_f32(hi >> 16) / s;
-  if constexpr (QT == kFp8) return f32x4_to_e4m3x4_sat(a, b, c, d);
-  return f32_to_i8_sat(a) | (f32_to_i8_sat(b) << 8) | (f32_to_i8_sat(c) << 16) | (f32_to_i8_sat(d) << 24);
-}
-
-template <int QT>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* x, int64_t numel, float s,
                                                         uint8_t* xq, int vec_ok) {
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -143,6 +135,73 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* x, int64
   for (int64_t i = nvec * 8 + tid; i < numel; i += stride) {
     float v = bf16_bits_to_f32(x[i]) / s;
     xq[i] = (uint8_t)(QT == kFp8 ? f32_to_e4m3_sat(v) : f32_to_i8_sat(v));
+  }
+}
+
+// Dynamic per-token quantization.  RPW rows per workgroup, T = 256 / RPW threads
+// per row.  Pass 1 reduces the row's absmax (x_scale[m] = absmax / qmax, 1 for
+// an all-zero row: the weight rule); pass 2 writes the codes.  On the vector path
+// (K % 8 == 0, 16-byte aligned rows) each thread keeps its first kCache 16-byte
+// chunks of the row in registers between the passes and re-reads the rest.
+template <int QT, int RPW>
+__global__ __launch_bounds__(256) void quant_act_dynamic_kernel(const uint16_t* x, int M, int K, uint8_t* xq,
+                                                                float* x_scale, int vec_ok) {
+  constexpr int T = 256 / RPW, kCache = 8, WPR = T / 64;    // threads and waves per row
+  const int tid = threadIdx.x, sub = tid / T, t = tid % T;
+  const int m = blockIdx.x * RPW + sub;
+  const bool live = m < M;
+  const uint16_t* row = x + (int64_t)(live ? m : 0) * K;
+  uint8_t* out = xq + (int64_t)(live ? m : 0) * K;
+  const int nvec = (vec_ok && live) ? K / 8 : 0;
+  u32x4 cache[kCache];
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kCache; ++j) {
+    const int i = t + j * T;
+    cache[j] = i < nvec ? ld16(row + i * 8) : (u32x4){0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < kCache; ++j) {
+    const uint32_t d[4] = {cache[j].x, cache[j].y, cache[j].z, cache[j].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      am = fmaxf(am, fmaxf(fabsf(bf16_bits_to_f32(d[c] & 0xFFFF)), fabsf(bf16_bits_to_f32(d[c] >> 16))));
+  }
+  for (int i = t + kCache * T; i < nvec; i += T) {
+    const u32x4 v = ld16(row + i * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      am = fmaxf(am, fmaxf(fabsf(bf16_bits_to_f32(d[c] & 0xFFFF)), fabsf(bf16_bits_to_f32(d[c] >> 16))));
+  }
+  if (live)
+    for (int k = nvec * 8 + t; k < K; k += T) am = fmaxf(am, fabsf(bf16_bits_to_f32(row[k])));
+  am = wave_max(am);
+  if constexpr (WPR > 1) {
+    __shared__ float red[RPW][WPR];
+    if ((tid & 63) == 0) red[sub][t >> 6] = am;
+    __syncthreads();
+    am = red[sub][0];
+#pragma unroll
+    for (int w = 1; w < WPR; ++w) am = fmaxf(am, red[sub][w]);
+  }
+  if (!live) return;
+  const float s = scale_of(am, QT == kFp8 ? 448.0f : 127.0f);
+  if (t == 0) x_scale[m] = s;
+#pragma unroll
+  for (int j = 0; j < kCache; ++j) {
+    const int i = t + j * T;
+    if (i < nvec)
+      *reinterpret_cast<u32x2*>(out + i * 8) =
+          (u32x2){quant4<QT>(cache[j].x, cache[j].y, s), quant4<QT>(cache[j].z, cache[j].w, s)};
+  }
+  for (int i = t + kCache * T; i < nvec; i += T) {
+    const u32x4 v = ld16(row + i * 8);
+    *reinterpret_cast<u32x2*>(out + i * 8) = (u32x2){quant4<QT>(v.x, v.y, s), quant4<QT>(v.z, v.w, s)};
+  }
+  for (int k = nvec * 8 + t; k < K; k += T) {
+    const float v = bf16_bits_to_f32(row[k]) / s;
+    out[k] = (uint8_t)(QT == kFp8 ? f32_to_e4m3_sat(v) : f32_to_i8_sat(v));
   }
 }
 
@@ -194,6 +253,28 @@ hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, vo
     quant_act_kernel<kFp8><<<grid, 256, 0, st>>>(xs, numel, s, out, vec_ok);
   else
     quant_act_kernel<kInt8><<<grid, 256, 0, st>>>(xs, numel, s, out, vec_ok);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_dynamic(const void* x, int M, int K, int qtype, void* xq, float* x_scale,
+                                   hipStream_t st) {
+  const int vec_ok = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(xq) & 7) == 0);
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
+  uint8_t* out = reinterpret_cast<uint8_t*>(xq);
+  // few rows: a whole workgroup per row; many rows: one wave per row
+  if (M < 1024) {
+    if (qtype == kFp8)
+      quant_act_dynamic_kernel<kFp8, 1><<<M, 256, 0, st>>>(xs, M, K, out, x_scale, vec_ok);
+    else
+      quant_act_dynamic_kernel<kInt8, 1><<<M, 256, 0, st>>>(xs, M, K, out, x_scale, vec_ok);
+  } else {
+    const int grid = (M + 3) / 4;
+    if (qtype == kFp8)
+      quant_act_dynamic_kernel<kFp8, 4><<<grid, 256, 0, st>>>(xs, M, K, out, x_scale, vec_ok);
+    else
+      quant_act_dynamic_kernel<kInt8, 4><<<grid, 256, 0, st>>>(xs, M, K, out, x_scale, vec_ok);
+  }
   return hipGetLastError();
 }
 
