@@ -25,6 +25,8 @@ Sources ("the pages"):
   absmax alternative it contrasts with is the dynamic scheme here).
 * "tiny-vLLM" README, section "Quantization Results" / "Quality Check":
   reconstruction error of the quantized weights (relative L2, cosine).
+* "Nano-vLLM-MoE" README, section "KV cache compression": the mixed K-int8
+  (group 32, fp16 scales) / V-FP8 per-token codec (``kvcache``).
 
 Parity status: every public function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, exhaustive codec checks against torch's casts, exact rational
@@ -38,6 +40,8 @@ from .qlinear import (qmax_of, weight_scale, quantize_weight, dequantize_weight_
                       calibrate_input_scale, quantize_act_static, quantize_act_dynamic,
                       qlinear_w8a16, w8a8_accumulate, w8a8_epilogue, qlinear_w8a8_static,
                       w8a8_epilogue_per_token, qlinear_w8a8_dynamic, reconstruction_error)
+from .kvcache import (K_GROUP, fp16_encode, fp16_decode, kv_quantize, kv_dequantize,
+                      kv_bytes_per_token_head)
 
 __all__ = [
     "bf16_bits_to_f32", "f32_to_bf16_bits", "bf16_round", "e4m3fn_decode",
@@ -45,5 +49,6 @@ __all__ = [
     "quantize_weight", "dequantize_weight_bf16", "calibrate_input_scale",
     "quantize_act_static", "quantize_act_dynamic", "qlinear_w8a16", "w8a8_accumulate",
     "w8a8_epilogue", "qlinear_w8a8_static", "w8a8_epilogue_per_token", "qlinear_w8a8_dynamic",
-    "reconstruction_error",
+    "reconstruction_error", "K_GROUP", "fp16_encode", "fp16_decode", "kv_quantize", "kv_dequantize",
+    "kv_bytes_per_token_head",
 ]
