@@ -18,9 +18,14 @@ as a HIP graph and replayed, so the timed region holds GPU work only; weights
 (1.65 GiB per variant) are far larger than the 256 MB last-level cache, so
 every step streams them from HBM.
 
-`next_rows` (not part of the step or of `value`): the same stack in INT8 W8A8
-with dynamic per-token activation scales (quantize_act_dynamic +
-qlinear_w8a8_dynamic per layer), timed the same way after the main region.
+`next_rows` (not part of the step or of `value`), timed the same way after the
+main region:
+  * the same stack in INT8 W8A8 with dynamic per-token activation scales
+    (quantize_act_dynamic + qlinear_w8a8_dynamic per layer);
+  * the mixed K-int8 / V-FP8 KV-cache codec on the 7B shape of the pages' KV
+    section (28 layers x 4 KV heads x head_dim 128): quantize T new tokens and
+    decode T cached tokens per layer, T from 1 to 32768 (the 32K context of
+    the pages' PPL table).
 
 Output: one JSON line on stdout.  `value` is the whole step's TFLOP/s (2 M N K
 per GEMM); `cases` gives us, TFLOP/s, algorithmic GB/s and roofline fractions per
@@ -127,6 +132,60 @@ def build_stack(qlq, synth, torch, dev, seed, layers):
             h = qlq.qlinear_w8a16(h, qf[l][p])
     sx = scales.cpu().tolist()
     return qi, qf, [[sx[3 * l + p] for p in range(3)] for l in range(layers)]
+
+
+KV_LAYERS, KV_HEADS, KV_DIM = 28, 4, 128
+KV_TOKENS = (1, 16, 256, 1024, 8192, 32768)     # new tokens per step up to a 32K context read
+
+
+def kv_rows(qlq, torch, dev, Ts, steps, warmup):
+    """Time the KV-cache codec: one graph per (op, T) over the 28 layers."""
+    import numpy as np
+    Tmax = max(Ts)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    shape = (KV_LAYERS, Tmax, KV_HEADS, KV_DIM)
+    k = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    q = [qlq.kv_quantize(k[l], v[l]) for l in range(KV_LAYERS)]
+    ko = torch.empty((Tmax, KV_HEADS, KV_DIM), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    per_entry = 2 * KV_DIM + 2 * (KV_DIM // 32) + 2
+    res = {}
+    stream = torch.cuda.Stream()
+    for op in ("kv_quantize", "kv_dequantize"):
+        for T in Ts:
+            def run():
+                for l in range(KV_LAYERS):
+                    if op == "kv_quantize":
+                        e = q[l]
+                        qlq.kv_quantize(k[l, :T], v[l, :T], out=qlq.QuantizedKV(e.k_codes[:T], e.k_scales[:T],
+                                                                                e.v_codes[:T], e.v_scales[:T]))
+                    else:
+                        e = q[l]
+                        qlq.kv_dequantize(qlq.QuantizedKV(e.k_codes[:T], e.k_scales[:T], e.v_codes[:T],
+                                                          e.v_scales[:T]), ko[:T], vo[:T])
+            run()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                run()
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps / KV_LAYERS
+            entries = T * KV_HEADS
+            byts = entries * (4 * KV_DIM + per_entry)             # bf16 K and V one way, codes + scales the other
+            res[f"{op}/T={T}"] = {"us_per_layer": round(us, 3), "gbs": round(byts / us / 1e3, 1),
+                                  "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 3), "bound": "hbm"}
+    return res
 
 
 def cpu_baseline(seed, layers_w, sx):
@@ -309,6 +368,7 @@ def main():
     groups = {}
     out_cases, tot_flops = figures(VARIANTS, groups)
     next_cases_out, _ = figures(NEXT_VARIANTS)
+    next_cases_out.update(kv_rows(qlq, torch, dev, KV_TOKENS, args.steps, args.warmup))
     # dominant kernel: the (variant, kernel family) group with the most time
     fam, g = max(groups.items(), key=lambda kv: kv[1]["us"])
     avg_us = g["us"] / g["launches"]
@@ -342,7 +402,8 @@ def main():
                        "layers": L, "M": list(Ms), "variants": [v[0] for v in VARIANTS],
                        "gemms_per_step": 3 * L * len(cases)},
             "cases": out_cases, "roofline": roof,
-            "next_rows": {"note": "INT8 W8A8 with dynamic per-token activation scales on the same stack; "
+            "next_rows": {"note": "INT8 W8A8 with dynamic per-token activation scales on the same stack, and "
+                                  "the mixed K-int8/V-FP8 KV-cache codec (28 layers x 4 KV heads x 128); "
                                   "timed after the step, not part of value or ms_per_step",
                           "cases": next_cases_out}}
     if args.copy_calibration:

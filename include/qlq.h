@@ -194,6 +194,32 @@ qlq_status qlq_qlinear_w8a8_dynamic(const void* xq, const float* x_scale,
                                     void* y, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* ---------------------------------------------------------------- KV cache */
+
+/* KV-cache codec: mixed K-int8 / V-FP8 dynamic per-token quantization ("Nano-vLLM-MoE"
+ * README, section "KV cache compression": mixed K int8 + V FP8, K group = 32, float16
+ * scales).  K and V are bf16 [T, H, D] (tokens, KV heads, head_dim), D a multiple of
+ * 32 (at most 1024).  Scales are IEEE binary16 bit patterns.
+ *   K, per (t, h, group g of channels 32g .. 32g+31):
+ *     k_scales[t,h,g] = fp16(absmax / 127)  (fp32 division, round to nearest even,
+ *                       saturating at 65504; 1 for an all-zero group; 2^-24 when a
+ *                       positive absmax would round to 0)
+ *     k_codes[t,h,d]  = clamp(round-to-nearest-even(k / fp32(k_scales)), -127, 127)
+ *   V, per (t, h): v_scales[t,h] = fp16(absmax_d |v[t,h,d]| / 448) (same rules),
+ *     v_codes[t,h,d] = e4m3fn_sat(round-to-nearest-even(v / fp32(v_scales)))
+ * k_codes int8 [T,H,D], k_scales [T,H,D/32], v_codes e4m3fn [T,H,D], v_scales [T,H].
+ * Per (t, h) this stores 2D + D/16 + 2 bytes: 0.5195 of bf16 at D = 128. */
+qlq_status qlq_kv_quantize(const void* k_bf16, const void* v_bf16, int64_t T, int64_t H, int64_t D,
+                           void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                           hipStream_t stream);
+
+/* Decoding for attention: k[t,h,d] = bf16(fp32(k_code) * fp32(k_scale of its group)),
+ * v[t,h,d] = bf16(fp32(v_code) * fp32(v_scale[t,h])).  Code buffers must be 8-byte
+ * aligned and the bf16 outputs 16-byte aligned. */
+qlq_status qlq_kv_dequantize(const void* k_codes, const void* k_scales, const void* v_codes,
+                             const void* v_scales, int64_t T, int64_t H, int64_t D,
+                             void* k_bf16, void* v_bf16, hipStream_t stream);
+
 /* ------------------------------------------------------------------- errors */
 
 const char* qlq_status_string(qlq_status status);

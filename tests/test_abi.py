@@ -160,3 +160,18 @@ def test_validation_of_the_next_rows():
     st, msg = _status(L.qlq_qlinear_w8a8_static_fused, FAKE, 1.0, 64, 128, 32, FAKE, FAKE, 32, 0, 0, FAKE,
                       ctypes.c_void_p(0x10010), need, None)
     assert st == 1 and "256-byte" in msg
+
+
+def test_validation_of_the_kv_codec():
+    L = qlq.lib()
+    assert "qlq_kv_quantize" in _declared() and "qlq_kv_dequantize" in _declared()
+    st, msg = _status(L.qlq_kv_quantize, FAKE, FAKE, 4, 2, 100, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 1 and "multiple of 32" in msg
+    st, msg = _status(L.qlq_kv_quantize, FAKE, None, 4, 2, 128, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 1 and "null" in msg
+    st, _ = _status(L.qlq_kv_quantize, FAKE, FAKE, 0, 2, 128, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 1
+    st, msg = _status(L.qlq_kv_dequantize, FAKE, FAKE, FAKE, FAKE, 4, 2, 2048, FAKE, FAKE, None)
+    assert st == 1 and "1024" in msg
+    st, msg = _status(L.qlq_kv_dequantize, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, ctypes.c_void_p(0x10008), FAKE, None)
+    assert st == 1 and "aligned" in msg

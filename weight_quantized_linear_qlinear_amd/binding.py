@@ -47,6 +47,10 @@ _SIGNATURES = {
     "qlq_qlinear_w8a8_dynamic": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
                                             _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
                                             _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_kv_quantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p,
+                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "qlq_kv_dequantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                                     _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "qlq_status_string": (_c.c_char_p, [_c.c_int]),
     "qlq_last_error": (_c.c_char_p, []),
     "qlq_version": (_c.c_char_p, []),
@@ -306,3 +310,42 @@ def qlinear_w8a8_dynamic(xq: torch.Tensor, x_scale: torch.Tensor, qw: QuantizedW
                                           _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
                                           _stream(xq.device)))
     return out
+
+
+# ---------------------------------------------------------------------- KV cache
+@dataclasses.dataclass
+class QuantizedKV:
+    """Mixed K-int8 / V-FP8 cache entries for [T, H, D] keys and values."""
+    k_codes: torch.Tensor     # int8 [T, H, D]
+    k_scales: torch.Tensor    # float16 [T, H, D / 32]
+    v_codes: torch.Tensor     # uint8 e4m3fn bits [T, H, D]
+    v_scales: torch.Tensor    # float16 [T, H]
+
+
+def kv_quantize(k: torch.Tensor, v: torch.Tensor, out: QuantizedKV | None = None) -> QuantizedKV:
+    """Quantize bf16 K and V [T, H, D] (D % 32 == 0) into cache entries."""
+    _require_gpu(k, v)
+    if k.dim() != 3 or k.shape != v.shape or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("k and v must be bf16 [T, H, D] of the same shape")
+    T, H, D = k.shape
+    if out is None:
+        out = QuantizedKV(torch.empty((T, H, D), dtype=torch.int8, device=k.device),
+                          torch.empty((T, H, max(D // 32, 1)), dtype=torch.float16, device=k.device),
+                          torch.empty((T, H, D), dtype=torch.uint8, device=k.device),
+                          torch.empty((T, H), dtype=torch.float16, device=k.device))
+    _check(lib().qlq_kv_quantize(_ptr(k), _ptr(v), T, H, D, _ptr(out.k_codes), _ptr(out.k_scales),
+                                 _ptr(out.v_codes), _ptr(out.v_scales), _stream(k.device)))
+    return out
+
+
+def kv_dequantize(q: QuantizedKV, k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None):
+    """Cache entries -> bf16 (K, V) [T, H, D]."""
+    _require_gpu(q.k_codes, q.k_scales, q.v_codes, q.v_scales)
+    T, H, D = q.k_codes.shape
+    if k_out is None:
+        k_out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.k_codes.device)
+    if v_out is None:
+        v_out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.k_codes.device)
+    _check(lib().qlq_kv_dequantize(_ptr(q.k_codes), _ptr(q.k_scales), _ptr(q.v_codes), _ptr(q.v_scales), T, H, D,
+                                   _ptr(k_out), _ptr(v_out), _stream(q.k_codes.device)))
+    return k_out, v_out

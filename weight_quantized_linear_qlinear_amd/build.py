@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlq.so")
 
-SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_small.hip", "gemm_large.hip", "gemm_mfma.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_small.hip", "gemm_large.hip", "gemm_mfma.hip", "kv_codec.hip"]
 ARCH = os.environ.get("QLQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -405,4 +405,36 @@ qlq_status qlq_qlinear_w8a8_dynamic(const void* xq, const float* x_scale, int64_
                   out == QLQ_OUT_ACC ? 1 : 0, y, workspace, workspace_bytes, stream, "qlinear_w8a8_dynamic");
 }
 
+static qlq_status check_kv_dims(int64_t T, int64_t H, int64_t D) {
+  if (T < 1 || H < 1 || D < 1) return fail(QLQ_ERR_INVALID_ARG, "T, H and D must be >= 1");
+  if (D % 32 != 0 || D > 1024) return fail(QLQ_ERR_INVALID_ARG, "head_dim D must be a multiple of 32, at most 1024");
+  if (T > kMaxDim || H > kMaxDim || T * H > kMaxDim) return fail(QLQ_ERR_INVALID_ARG, "T * H too large");
+  return QLQ_OK;
+}
+
+qlq_status qlq_kv_quantize(const void* k_bf16, const void* v_bf16, int64_t T, int64_t H, int64_t D, void* k_codes,
+                           void* k_scales, void* v_codes, void* v_scales, hipStream_t stream) {
+  if (!k_bf16 || !v_bf16 || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_kv_dims(T, H, D)) return st;
+  if (!aligned(k_bf16, 2) || !aligned(v_bf16, 2) || !aligned(k_scales, 2) || !aligned(v_scales, 2))
+    return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(qlq::launch_kv_quantize(k_bf16, v_bf16, T * H, (int)D, k_codes, k_scales, v_codes, v_scales,
+                                            stream),
+                    "kv_quantize");
+}
+
+qlq_status qlq_kv_dequantize(const void* k_codes, const void* k_scales, const void* v_codes, const void* v_scales,
+                             int64_t T, int64_t H, int64_t D, void* k_bf16, void* v_bf16, hipStream_t stream) {
+  if (!k_bf16 || !v_bf16 || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_kv_dims(T, H, D)) return st;
+  if (!aligned(k_codes, 8) || !aligned(v_codes, 8) || !aligned(k_bf16, 16) || !aligned(v_bf16, 16) ||
+      !aligned(k_scales, 2) || !aligned(v_scales, 2))
+    return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer (codes 8-byte, outputs 16-byte aligned)");
+  return hip_status(qlq::launch_kv_dequantize(k_codes, k_scales, v_codes, v_scales, T * H * D, (int)D, k_bf16,
+                                              v_bf16, stream),
+                    "kv_dequantize");
+}
+
 }  // extern "C"

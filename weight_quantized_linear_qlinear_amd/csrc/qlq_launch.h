@@ -63,6 +63,10 @@ hipError_t launch_pack_weight(const void* w, int is_bf16, int N, int K, int qtyp
                               uint8_t* packed, float* w_scale, hipStream_t st);
 hipError_t launch_unpack_weight(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st);
 hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st);
+hipError_t launch_kv_quantize(const void* k, const void* v, int64_t rows, int D, void* kq, void* ks, void* vq,
+                              void* vs, hipStream_t st);
+hipError_t launch_kv_dequantize(const void* kq, const void* ks, const void* vq, const void* vs, int64_t numel, int D,
+                                void* ko, void* vo, hipStream_t st);
 hipError_t launch_quant_act_dynamic(const void* x, int M, int K, int qtype, void* xq, float* x_scale,
                                    hipStream_t st);
 
