@@ -39,7 +39,7 @@ from .codecs import (bf16_bits_to_f32, f32_to_bf16_bits, bf16_round,
 from .qlinear import (qmax_of, weight_scale, quantize_weight, dequantize_weight_bf16,
                       calibrate_input_scale, quantize_act_static, quantize_act_dynamic,
                       qlinear_w8a16, w8a8_accumulate, w8a8_epilogue, qlinear_w8a8_static,
-                      w8a8_epilogue_per_token, qlinear_w8a8_dynamic, reconstruction_error)
+                      w8a8_epilogue_per_token, qlinear_w8a8_dynamic, linear, reconstruction_error)
 from .kvcache import (K_GROUP, fp16_encode, fp16_decode, kv_quantize, kv_dequantize,
                       kv_bytes_per_token_head)
 
@@ -49,6 +49,6 @@ __all__ = [
     "quantize_weight", "dequantize_weight_bf16", "calibrate_input_scale",
     "quantize_act_static", "quantize_act_dynamic", "qlinear_w8a16", "w8a8_accumulate",
     "w8a8_epilogue", "qlinear_w8a8_static", "w8a8_epilogue_per_token", "qlinear_w8a8_dynamic",
-    "reconstruction_error", "K_GROUP", "fp16_encode", "fp16_decode", "kv_quantize", "kv_dequantize",
+    "linear", "reconstruction_error", "K_GROUP", "fp16_encode", "fp16_decode", "kv_quantize", "kv_dequantize",
     "kv_bytes_per_token_head",
 ]

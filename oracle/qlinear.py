@@ -30,7 +30,10 @@ Readings where the pages are silent (each is listed in the design doc):
   quantizer's rule on that row alone: s_x[m] = absmax(x[m, :]) / qmax (1.0
   for an all-zero row) and xq = sat(RNE(x / s_x[m])); its epilogue is the
   static one with s_x replaced by s_x[m]:
-  y = bf16(fp32(acc) * fp32(s_x[m] * s_w[n])).
+  y = bf16(fp32(acc) * fp32(s_x[m] * s_w[n]));
+* an optional bias b[n] (bf16, as the q/k/v projections of Qwen2-family models
+  carry) is added in fp32 after the scale epilogue, before the bf16 rounding:
+  y = bf16(fp32(v + b[n])) with v the fp32 value the epilogue would round.
 """
 from __future__ import annotations
 
@@ -130,13 +133,21 @@ def quantize_act_dynamic(x_bf16: np.ndarray, qtype: str):
     return q, s
 
 
+def _add_bias(v_f32: np.ndarray, bias_bf16) -> np.ndarray:
+    """fp32(v + b[n]) for a bf16 bias [N] (no bias: v unchanged)."""
+    if bias_bf16 is None:
+        return v_f32
+    b = bf16_bits_to_f32(np.asarray(bias_bf16, dtype=np.uint16)).reshape(1, -1)
+    return (v_f32 + b).astype(np.float32)
+
+
 def qlinear_w8a16(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray,
-                  qtype: str) -> np.ndarray:
-    """Weight-only quantized linear: y = bf16(fp32(sum_k x[m,k] * wd[n,k])), bf16 bits [M, N]."""
+                  qtype: str, bias_bf16=None) -> np.ndarray:
+    """Weight-only quantized linear: y = bf16(fp32(sum_k x[m,k] * wd[n,k]) [+ b[n]]), bf16 bits [M, N]."""
     x = bf16_bits_to_f32(x_bf16).astype(np.float64)
     wd = dequantize_weight_bf16(codes, scales, qtype).astype(np.float64)
     acc = x @ wd.T
-    return f32_to_bf16_bits(acc.astype(np.float32))
+    return f32_to_bf16_bits(_add_bias(acc.astype(np.float32), bias_bf16))
 
 
 def w8a8_accumulate(xq: np.ndarray, codes: np.ndarray, qtype: str) -> np.ndarray:
@@ -155,11 +166,11 @@ def w8a8_accumulate(xq: np.ndarray, codes: np.ndarray, qtype: str) -> np.ndarray
     return acc.astype(np.float32)
 
 
-def w8a8_epilogue(acc: np.ndarray, input_scale, scales: np.ndarray) -> np.ndarray:
-    """y = bf16(fp32(acc) * fp32(s_x * s_w[n])), bf16 bits [M, N]."""
+def w8a8_epilogue(acc: np.ndarray, input_scale, scales: np.ndarray, bias_bf16=None) -> np.ndarray:
+    """y = bf16(fp32(acc) * fp32(s_x * s_w[n]) [+ b[n]]), bf16 bits [M, N]."""
     comb = (np.float32(input_scale) * np.asarray(scales, dtype=np.float32)).astype(np.float32)
     accf = np.asarray(acc).astype(np.float32)
-    return f32_to_bf16_bits((accf * comb.reshape(1, -1)).astype(np.float32))
+    return f32_to_bf16_bits(_add_bias((accf * comb.reshape(1, -1)).astype(np.float32), bias_bf16))
 
 
 def qlinear_w8a8_static(xq: np.ndarray, input_scale, codes: np.ndarray, scales: np.ndarray,
@@ -179,12 +190,13 @@ def qlinear_w8a8_static(xq: np.ndarray, input_scale, codes: np.ndarray, scales: 
     return w8a8_epilogue(acc, input_scale, scales)
 
 
-def w8a8_epilogue_per_token(acc: np.ndarray, x_scale: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """y[m, n] = bf16(fp32(acc[m, n]) * fp32(s_x[m] * s_w[n])), bf16 bits [M, N]."""
+def w8a8_epilogue_per_token(acc: np.ndarray, x_scale: np.ndarray, scales: np.ndarray,
+                            bias_bf16=None) -> np.ndarray:
+    """y[m, n] = bf16(fp32(acc[m, n]) * fp32(s_x[m] * s_w[n]) [+ b[n]]), bf16 bits [M, N]."""
     sx = np.asarray(x_scale, dtype=np.float32).reshape(-1, 1)
     comb = (sx * np.asarray(scales, dtype=np.float32).reshape(1, -1)).astype(np.float32)
     accf = np.asarray(acc).astype(np.float32)
-    return f32_to_bf16_bits((accf * comb).astype(np.float32))
+    return f32_to_bf16_bits(_add_bias((accf * comb).astype(np.float32), bias_bf16))
 
 
 def qlinear_w8a8_dynamic(xq: np.ndarray, x_scale: np.ndarray, codes: np.ndarray, scales: np.ndarray,
@@ -197,6 +209,30 @@ def qlinear_w8a8_dynamic(xq: np.ndarray, x_scale: np.ndarray, codes: np.ndarray,
     if out == "acc":
         return qlinear_w8a8_static(xq, 1.0, codes, scales, qtype, out="acc")
     return w8a8_epilogue_per_token(w8a8_accumulate(xq, codes, qtype), x_scale, scales)
+
+
+def linear(scheme: str, x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray, qtype: str,
+           input_scale=None, bias_bf16=None, bf16_fallback_max_m: int = 0) -> np.ndarray:
+    """The routed quantized Linear from bf16 x: bf16 bits [M, N].
+
+    scheme "w8a16": qlinear_w8a16.  "w8a8_static": quantize_act_static with
+    input_scale, then the static GEMM.  "w8a8_dynamic": per-token quantization,
+    then the dynamic GEMM.  With bf16_fallback_max_m > 0, a W8A8 call with
+    M <= bf16_fallback_max_m skips activation quantization and computes the
+    W8A16 result on the same weight codes and scales (the small-batch BF16
+    fallback of the INT8 key-design list; it changes the numerics, so it is opt-in).
+    A bias is added in fp32 after the scale epilogue, before the bf16 rounding.
+    """
+    M = np.asarray(x_bf16).shape[0]
+    if scheme == "w8a16" or (bf16_fallback_max_m > 0 and M <= bf16_fallback_max_m):
+        return qlinear_w8a16(x_bf16, codes, scales, qtype, bias_bf16)
+    if scheme == "w8a8_static":
+        xq = quantize_act_static(x_bf16, input_scale, qtype)
+        return w8a8_epilogue(w8a8_accumulate(xq, codes, qtype), input_scale, scales, bias_bf16)
+    if scheme == "w8a8_dynamic":
+        xq, sx = quantize_act_dynamic(x_bf16, qtype)
+        return w8a8_epilogue_per_token(w8a8_accumulate(xq, codes, qtype), sx, scales, bias_bf16)
+    raise ValueError(scheme)
 
 
 def reconstruction_error(w: np.ndarray, codes: np.ndarray, scales: np.ndarray, qtype: str):

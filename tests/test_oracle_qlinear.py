@@ -461,3 +461,61 @@ def test_w8a8_dynamic_accumulator_is_the_static_one():
     acc = oracle.qlinear_w8a8_dynamic(xq, sx, q, s, "int8", out="acc")
     ref = xq.astype(np.int64) @ q.astype(np.int64).T            # numpy integer matmul
     assert acc.dtype == np.int32 and np.array_equal(acc.astype(np.int64), ref)
+
+
+# ---------------------------------------------------------------- routed Linear: bias and fallback
+def _bias_bits(seed, N):
+    rng = np.random.default_rng(seed)
+    return oracle.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.5))
+
+
+@pytest.mark.parametrize("scheme", ["w8a16", "w8a8_static", "w8a8_dynamic"])
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_linear_bias_bruteforce(scheme, qtype):
+    w, calib, x = synth.small_inputs(61, 3, 8, 5)
+    gran = "per_tensor" if (qtype != "int8" and scheme != "w8a16") else "per_channel"
+    q, s = oracle.quantize_weight(w, qtype, gran)
+    sx = oracle.calibrate_input_scale(calib, qtype)
+    b = _bias_bits(62, 5)
+    y = oracle.linear(scheme, x, q, s, qtype, input_scale=sx, bias_bf16=b)
+    xf = oracle.bf16_bits_to_f32(x)
+    if scheme == "w8a8_static":
+        xq, rows = oracle.quantize_act_static(x, sx, qtype), [Fraction(float(sx))] * 3
+    elif scheme == "w8a8_dynamic":
+        xq, sxr = oracle.quantize_act_dynamic(x, qtype)
+        rows = [Fraction(float(v)) for v in sxr]
+    wd = oracle.dequantize_weight_bf16(q, s, qtype)
+    for m in range(3):
+        for n in range(5):
+            bn = Fraction(float(oracle.bf16_bits_to_f32(b[n:n + 1])[0]))
+            if scheme == "w8a16":
+                v = exact.f32(sum(Fraction(float(xf[m, k])) * Fraction(float(wd[n, k])) for k in range(8)))
+            else:
+                acc = sum(_code_value(xq[m, k], qtype) * _code_value(q[n, k], qtype) for k in range(8))
+                comb = exact.f32(rows[m] * Fraction(float(s[n if s.size > 1 else 0])))
+                v = exact.f32(exact.f32(acc) * comb)
+            assert y[m, n] == exact.bf16_bits_of(exact.bf16(exact.f32(v + bn)))
+
+
+def test_linear_zero_bias_changes_nothing_and_zero_x_gives_the_bias():
+    w, calib, x = synth.small_inputs(63, 4, 64, 16)
+    q, s = oracle.quantize_weight(w, "int8")
+    sx = oracle.calibrate_input_scale(calib, "int8")
+    zero = np.zeros(16, np.uint16)
+    for scheme in ["w8a16", "w8a8_static", "w8a8_dynamic"]:
+        y0 = oracle.linear(scheme, x, q, s, "int8", input_scale=sx)
+        assert np.array_equal(oracle.linear(scheme, x, q, s, "int8", input_scale=sx, bias_bf16=zero), y0)
+        b = _bias_bits(64, 16)
+        yb = oracle.linear(scheme, np.zeros_like(x), q, s, "int8", input_scale=sx, bias_bf16=b)
+        assert np.array_equal(yb, np.broadcast_to(b, yb.shape))      # bf16 bias survives exactly
+
+
+def test_linear_bf16_fallback_is_the_weight_only_result_and_differs_from_w8a8():
+    w, calib, x = synth.small_inputs(65, 32, 512, 64)
+    q, s = oracle.quantize_weight(w, "int8")
+    sx = oracle.calibrate_input_scale(calib, "int8")
+    y_fb = oracle.linear("w8a8_static", x, q, s, "int8", input_scale=sx, bf16_fallback_max_m=32)
+    assert np.array_equal(y_fb, oracle.qlinear_w8a16(x, q, s, "int8"))
+    y_q = oracle.linear("w8a8_static", x, q, s, "int8", input_scale=sx, bf16_fallback_max_m=16)
+    assert np.array_equal(y_q, oracle.qlinear_w8a8_static(oracle.quantize_act_static(x, sx, "int8"), sx, q, s, "int8"))
+    assert not np.array_equal(y_fb, y_q)                               # the fallback changes the numerics
