@@ -22,6 +22,8 @@ every step streams them from HBM.
 main region:
   * the same stack in INT8 W8A8 with dynamic per-token activation scales
     (quantize_act_dynamic + qlinear_w8a8_dynamic per layer);
+  * the same stack through the routed Linear (qlq_linear: INT8 dynamic W8A8,
+    a bf16 bias per projection, BF16 fallback for M <= 32);
   * the mixed K-int8 / V-FP8 KV-cache codec on the 7B shape of the pages' KV
     section (28 layers x 4 KV heads x head_dim 128): quantize T new tokens and
     decode T cached tokens per layer, T from 1 to 32768 (the 32K context of
@@ -51,7 +53,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
 VARIANTS = (("int8_w8a16", "w8a16", "int8", "per_channel"),
             ("fp8_w8a8_static", "w8a8_static_fused", "fp8_e4m3fn", "per_tensor"))
-NEXT_VARIANTS = (("int8_w8a8_dynamic", "w8a8_dynamic", "int8", "per_channel"),)
+NEXT_VARIANTS = (("int8_w8a8_dynamic", "w8a8_dynamic", "int8", "per_channel"),
+                 ("int8_linear_routed", "linear_routed", "int8", "per_channel"))
 
 
 def log(*a):
@@ -74,6 +77,10 @@ def gemm_bytes(scheme, M, K, N, per_tensor):
         return N * K + scale + 4 * M * K + 2 * M * N
     if scheme == "w8a8_dynamic":
         return N * K + scale + 4 * M * K + 8 * M + 2 * M * N
+    if scheme == "linear_routed":      # dynamic W8A8 + bias; BF16 fallback (W8A16 bytes) at M <= 32
+        if M <= 32:
+            return N * K + scale + 2 * M * K + 2 * M * N + 2 * N
+        return N * K + scale + 4 * M * K + 8 * M + 2 * M * N + 2 * N
     return N * K + scale + M * K + 2 * M * N
 
 
@@ -250,7 +257,12 @@ def main():
     torch.cuda.set_device(dev)
     L = args.layers
     qi, qf, sx = build_stack(qlq, synth, torch, dev, args.seed, L)
-    variants = {"int8_w8a16": qi, "fp8_w8a8_static": qf, "int8_w8a8_dynamic": qi}
+    variants = {"int8_w8a16": qi, "fp8_w8a8_static": qf, "int8_w8a8_dynamic": qi, "int8_linear_routed": qi}
+    # routed Linear: a bf16 bias per layer and projection, BF16 fallback at M <= 32
+    gb = torch.Generator(device=dev)
+    gb.manual_seed(args.seed + 77)
+    biases = [[(torch.randn(N, generator=gb, device=dev) * 0.1).to(torch.bfloat16) for _, _, N in synth.STACK_PROJS]
+              for _ in range(L)]
 
     # buffers: inputs per M, ping-pong activations, codes, one shared workspace
     Ms = synth.STACK_M
@@ -266,7 +278,10 @@ def main():
     for _, scheme, qtype, _ in VARIANTS + NEXT_VARIANTS:
         for M in Ms:
             for _, K, N in synth.STACK_PROJS:
-                ws_need = max(ws_need, qlq.workspace_bytes(scheme, M, K, N, qtype))
+                if scheme == "linear_routed":
+                    ws_need = max(ws_need, qlq.linear_workspace_bytes("w8a8_dynamic", M, K, N, qtype))
+                else:
+                    ws_need = max(ws_need, qlq.workspace_bytes(scheme, M, K, N, qtype))
     ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
 
     scheme_of = {v[0]: v[1] for v in VARIANTS + NEXT_VARIANTS}
@@ -283,6 +298,9 @@ def main():
                     qlq.qlinear_w8a16(h, qw, out=out, workspace=ws)
                 elif scheme == "w8a8_static_fused":
                     qlq.qlinear_w8a8_static_fused(h, sx[l][p], qw, out=out, workspace=ws)
+                elif scheme == "linear_routed":
+                    qlq.linear("w8a8_dynamic", h, qw, bias=biases[l][p], bf16_fallback_max_m=32, out=out,
+                               workspace=ws)
                 else:
                     xq, xs = qlq.quantize_act_dynamic(h, "int8", out=xqbuf[: M * K].view(M, K), x_scale=sxbuf[:M])
                     qlq.qlinear_w8a8_dynamic(xq, xs, qw, out=out, workspace=ws)
@@ -346,7 +364,8 @@ def main():
                 us = sum(a.elapsed_time(b) for a, b in ev[(vname, M)]) * 1e3 / args.steps
                 flops = sum(2 * M * N * K for _, K, N in synth.STACK_PROJS) * L
                 byts = sum(gemm_bytes(scheme, M, K, N, gran == "per_tensor") for _, K, N in synth.STACK_PROJS) * L
-                dt = "bf16" if scheme == "w8a16" else ("fp8" if qtype == "fp8_e4m3fn" else "int8")
+                dt = "bf16" if (scheme == "w8a16" or (scheme == "linear_routed" and M <= 32)) else \
+                    ("fp8" if qtype == "fp8_e4m3fn" else "int8")
                 t_hbm = byts / (HBM_PEAK_GBS * 1e9) * 1e6
                 t_mfma = flops / (MFMA_PEAK_TFLOPS[dt] * 1e12) * 1e6
                 flops_all += flops

@@ -194,6 +194,33 @@ qlq_status qlq_qlinear_w8a8_dynamic(const void* xq, const float* x_scale,
                                     void* y, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* ------------------------------------------------------------ routed Linear */
+
+/* The quantized Linear as a serving engine routes it by its checkpoint's scheme
+ * (the quantization_type routing of the INT8 section's quick-start): y bf16 [M, N]
+ * from bf16 x [M, K], with an optional bias and the opt-in small-batch fallback.
+ *   scheme QLQ_SCHEME_W8A16         qlq_qlinear_w8a16
+ *          QLQ_SCHEME_W8A8_STATIC   quantize with input_scale, then the static GEMM
+ *          QLQ_SCHEME_W8A8_DYNAMIC  per-token quantization, then the dynamic GEMM
+ *   bias_bf16            bf16 [N] or NULL: y = bf16(fp32(v + bias[n])), v the fp32
+ *                        value the scale epilogue would round (added in fp32, not fused
+ *                        with the product)
+ *   bf16_fallback_max_m  W8A8 schemes: M <= this skips activation quantization and
+ *                        computes the W8A16 result on the same weight codes and
+ *                        scales (the key-design list's BF16 fallback for small
+ *                        batches, 32 there); it changes the numerics, so 0 (off) is
+ *                        the neutral value
+ * The activation codes (and per-token scales) live in the workspace; size it with
+ * qlq_linear_workspace_bytes (zero-fill rule as for every workspace). */
+qlq_status qlq_linear(qlq_scheme scheme, const void* x_bf16, int64_t M, int64_t K, int64_t N,
+                      const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                      qlq_qtype qtype, float input_scale, const void* bias_bf16,
+                      int64_t bf16_fallback_max_m, void* y_bf16, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of qlq_linear for these sizes (covers the fallback too). */
+size_t qlq_linear_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype);
+
 /* ---------------------------------------------------------------- KV cache */
 
 /* KV-cache codec: mixed K-int8 / V-FP8 dynamic per-token quantization ("Nano-vLLM-MoE"

@@ -175,3 +175,30 @@ def test_validation_of_the_kv_codec():
     assert st == 1 and "1024" in msg
     st, msg = _status(L.qlq_kv_dequantize, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, ctypes.c_void_p(0x10008), FAKE, None)
     assert st == 1 and "aligned" in msg
+
+
+def test_validation_of_the_routed_linear():
+    L = qlq.lib()
+    for n in ["qlq_linear", "qlq_linear_workspace_bytes"]:
+        assert n in _declared()
+    st, msg = _status(L.qlq_linear, 2, FAKE, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, None, 0, FAKE, None, 0, None)
+    assert st == 2 and "scheme" in msg
+    st, msg = _status(L.qlq_linear, 1, FAKE, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, None, -1, FAKE, None, 0, None)
+    assert st == 1 and "fallback" in msg
+    st, msg = _status(L.qlq_linear, 1, FAKE, 4, 64, 16, FAKE, FAKE, 16, 0, float("nan"), None, 0, FAKE, None, 0, None)
+    assert st == 1 and "input_scale" in msg
+    need = qlq.linear_workspace_bytes("w8a8_dynamic", 4, 64, 16, "int8")
+    st, msg = _status(L.qlq_linear, 3, FAKE, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, None, 0, FAKE, FAKE, need - 1, None)
+    assert st == 1 and "workspace" in msg
+    st, msg = _status(L.qlq_linear, 0, FAKE, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, ctypes.c_void_p(0x10001), 0, FAKE,
+                      None, 0, None)
+    assert st == 1 and "aligned" in msg
+
+
+def test_routed_linear_workspace_sizes():
+    for M, K, N in [(1, 2048, 2048), (16, 2048, 11008), (256, 11008, 2048), (1024, 2048, 11008)]:
+        assert qlq.linear_workspace_bytes("w8a16", M, K, N, "int8") == qlq.workspace_bytes("w8a16", M, K, N, "int8")
+        s = qlq.linear_workspace_bytes("w8a8_static", M, K, N, "int8")
+        d = qlq.linear_workspace_bytes("w8a8_dynamic", M, K, N, "int8")
+        assert s >= qlq.workspace_bytes("w8a8_static", M, K, N, "int8") + M * K and d >= s + 4 * M
+        assert s >= qlq.workspace_bytes("w8a16", M, K, N, "int8")          # the fallback fits too

@@ -51,6 +51,10 @@ _SIGNATURES = {
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "qlq_kv_dequantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                      _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "qlq_linear": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                              _c.c_int64, _c.c_int, _c.c_float, _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                              _c.c_size_t, _c.c_void_p]),
+    "qlq_linear_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "qlq_status_string": (_c.c_char_p, [_c.c_int]),
     "qlq_last_error": (_c.c_char_p, []),
     "qlq_version": (_c.c_char_p, []),
@@ -309,6 +313,37 @@ def qlinear_w8a8_dynamic(xq: torch.Tensor, x_scale: torch.Tensor, qw: QuantizedW
                                           _ptr(qw.scale), qw.scale.numel(), _qtype(qw.qtype), OUTS[out_mode],
                                           _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
                                           _stream(xq.device)))
+    return out
+
+
+# ---------------------------------------------------------------------- routed Linear
+LINEAR_SCHEMES = {"w8a16": 0, "w8a8_static": 1, "w8a8_dynamic": 3}
+
+
+def linear_workspace_bytes(scheme: str, M: int, K: int, N: int, qtype: str) -> int:
+    return int(lib().qlq_linear_workspace_bytes(LINEAR_SCHEMES[scheme], M, K, N, _qtype(qtype)))
+
+
+def linear(scheme: str, x: torch.Tensor, qw: QuantizedWeight, input_scale: float = 1.0,
+           bias: torch.Tensor | None = None, bf16_fallback_max_m: int = 0, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed quantized Linear: bf16 x [M, K] -> bf16 y [M, N] (+ bf16 bias [N])."""
+    _require_gpu(x)
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.shape[1] != qw.K:
+        raise ValueError(f"x must be bf16 [M, {qw.K}]")
+    if bias is not None:
+        _require_gpu(bias)
+        if bias.dtype != torch.bfloat16 or bias.numel() != qw.N:
+            raise ValueError(f"bias must be bf16 [{qw.N}]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, qw.N), dtype=torch.bfloat16, device=x.device)
+    nbytes = linear_workspace_bytes(scheme, M, qw.K, qw.N, qw.qtype)
+    ws = workspace if workspace is not None else _workspace(x.device, nbytes)
+    _check(lib().qlq_linear(LINEAR_SCHEMES[scheme], _ptr(x), M, qw.K, qw.N, _ptr(qw.packed), _ptr(qw.scale),
+                            qw.scale.numel(), _qtype(qw.qtype), float(input_scale), _ptr(bias),
+                            int(bf16_fallback_max_m), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                            _stream(x.device)))
     return out
 
 

@@ -295,7 +295,8 @@ qlq_status qlq_quantize_act_dynamic(const void* x_bf16, int64_t M, int64_t K, ql
 static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int64_t N, const void* wq_packed,
                            const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
                            const float* row_scale, int out_acc, void* y, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream, const char* what) {
+                           size_t workspace_bytes, hipStream_t stream, const char* what,
+                           const void* bias = nullptr) {
   if (!x || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
   if (qlq_status st = check_dims(M, K, N)) return st;
   if (qlq_status st = check_qtype(qtype)) return st;
@@ -304,7 +305,7 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
                 (long long)N);
   if (!aligned(wq_packed, 16)) return fail(QLQ_ERR_INVALID_ARG, "wq_packed must be 16-byte aligned");
   if (!aligned(w_scale, 4) || !aligned(y, 4) || !aligned(x, scheme == qlq::kW8A16 ? 2 : 1) ||
-      !aligned(row_scale, 4))
+      !aligned(row_scale, 4) || !aligned(bias, 2))
     return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
   const bool fast = (K % 64 == 0) && aligned(x, 16);
   qlq::GemmPlan plan = qlq::plan_gemm(scheme, (int)qtype, M, K, N, fast);
@@ -333,6 +334,7 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.NT = (int)cdiv(N, 16);
   a.input_scale = input_scale;
   a.row_scale = row_scale;
+  a.bias = static_cast<const uint16_t*>(bias);
   a.out_acc = out_acc;
   a.fast = fast;
   hipError_t e = plan.kind == 0   ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
@@ -435,6 +437,62 @@ qlq_status qlq_kv_dequantize(const void* k_codes, const void* k_scales, const vo
   return hip_status(qlq::launch_kv_dequantize(k_codes, k_scales, v_codes, v_scales, T * H * D, (int)D, k_bf16,
                                               v_bf16, stream),
                     "kv_dequantize");
+}
+
+// Routed Linear: workspace layout [GEMM region][codes M*K][row scales 4M], the
+// codes at the same offset as the fused static call (never below the counters).
+static size_t linear_codes_offset(int64_t M, int64_t K, int64_t N, int qtype) {
+  return fused_xq_offset(M, K, N, qtype);
+}
+
+size_t qlq_linear_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype) {
+  if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
+  const size_t w16 = gemm_ws_bytes(qlq::kW8A16, M, K, N, (int)qtype);
+  if (scheme == QLQ_SCHEME_W8A16) return w16;
+  if (scheme != QLQ_SCHEME_W8A8_STATIC && scheme != QLQ_SCHEME_W8A8_DYNAMIC) return 0;
+  size_t need = linear_codes_offset(M, K, N, (int)qtype) + ((size_t)M * (size_t)K + 255) / 256 * 256 +
+                (scheme == QLQ_SCHEME_W8A8_DYNAMIC ? (size_t)M * 4 : 0);
+  return need > w16 ? need : w16;           // the BF16 fallback runs the W8A16 GEMM in the same buffer
+}
+
+qlq_status qlq_linear(qlq_scheme scheme, const void* x_bf16, int64_t M, int64_t K, int64_t N, const void* wq_packed,
+                      const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
+                      const void* bias_bf16, int64_t bf16_fallback_max_m, void* y_bf16, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (scheme != QLQ_SCHEME_W8A16 && scheme != QLQ_SCHEME_W8A8_STATIC && scheme != QLQ_SCHEME_W8A8_DYNAMIC)
+    return fail(QLQ_ERR_UNSUPPORTED, "qlq_linear: unknown scheme %d", (int)scheme);
+  if (bf16_fallback_max_m < 0) return fail(QLQ_ERR_INVALID_ARG, "bf16_fallback_max_m must be >= 0");
+  if (scheme == QLQ_SCHEME_W8A8_STATIC)
+    if (qlq_status st = check_scale(input_scale, "input_scale")) return st;
+  if (scheme == QLQ_SCHEME_W8A16 || M <= bf16_fallback_max_m)
+    return run_gemm(qlq::kW8A16, x_bf16, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, 1.0f, nullptr, 0,
+                    y_bf16, workspace, workspace_bytes, stream, "linear", bias_bf16);
+  if (qlq_status st = check_w8a8(qtype, QLQ_OUT_BF16, K)) return st;
+  if (!x_bf16 || !wq_packed || !w_scale || !y_bf16) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(M, K, N)) return st;
+  if (!aligned(x_bf16, 2)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
+  const size_t need = qlq_linear_workspace_bytes(scheme, M, K, N, qtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(QLQ_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t off = linear_codes_offset(M, K, N, (int)qtype);
+  void* xq = static_cast<uint8_t*>(workspace) + off;
+  const float* rows = nullptr;
+  if (scheme == QLQ_SCHEME_W8A8_STATIC) {
+    if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream), "linear"))
+      return st;
+  } else {
+    float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(xq) + ((size_t)M * (size_t)K + 255) / 256 * 256);
+    if (qlq_status st = hip_status(qlq::launch_quant_act_dynamic(x_bf16, (int)M, (int)K, (int)qtype, xq, xs, stream),
+                                   "linear"))
+      return st;
+    rows = xs;
+  }
+  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype,
+                  scheme == QLQ_SCHEME_W8A8_STATIC ? input_scale : 1.0f, rows, 0, y_bf16, workspace, off, stream,
+                  "linear", bias_bf16);
 }
 
 }  // extern "C"

@@ -296,14 +296,14 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
         if (m >= a.M) continue;
         const int64_t o = (int64_t)m * a.N + n;
         if constexpr (SCH == kW8A16) {
-          reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)accf[i][j][jj];
+          reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(accf[i][j][jj], a.bias, n);
         } else if (a.out_acc) {
           if constexpr (T::kIntAcc) reinterpret_cast<int32_t*>(a.y)[o] = acci[i][j][jj];
           else reinterpret_cast<float*>(a.y)[o] = accf[i][j][jj];
         } else {
           const float v = T::kIntAcc ? (float)acci[i][j][jj] : accf[i][j][jj];
           const float comb = (a.row_scale ? a.row_scale[m] : a.input_scale) * sw;   // fp32(s_x * s_w[n])
-          reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
+          reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(v * comb, a.bias, n);
         }
       }
   }

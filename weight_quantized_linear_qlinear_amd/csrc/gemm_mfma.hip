@@ -400,6 +400,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
       rf[i] = a.input_scale;
       if (SCH == kW8A8 && a.row_scale) rf[i] = m < a.M ? a.row_scale[m] : 0.0f;
     }
+    // bias of this lane's columns (bf16 -> fp32, exact); zero without a bias
+    f32x4 bs[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bs[j][g] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        const int n = nt0 * 16 + (wn * TN + j) * 32 + 8 * g + 4 * kg;
+        if (a.bias && n < a.N) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) bs[j][g][c] = bf16_bits_to_f32(a.bias[n + c]);
+        }
+      }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -412,6 +425,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
           for (int c = 0; c < 4; ++c) {
             if constexpr (SCH == kW8A16) v[c] = accf[i][j][4 * g + c];
             else v[c] = (T::kIntAcc ? (float)acci[i][j][4 * g + c] : accf[i][j][4 * g + c]) * (rf[i] * sw[j][g][c]);
+            if (a.bias) v[c] = add_bias_value(v[c], bs[j][g][c]);
           }
           const int row = (wm * TM + i) * 32 + l32;
           *reinterpret_cast<u32x2*>(smem + row * PITCH + col * 2) = pack_bf16x4(v);
@@ -449,7 +463,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
           if (n >= a.N) continue;
           const int64_t o = (int64_t)m * a.N + n;
           if constexpr (SCH == kW8A16) {
-            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)accf[i][j][e];
+            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(accf[i][j][e], a.bias, n);
           } else if (a.out_acc) {
             if constexpr (T::kIntAcc) reinterpret_cast<int32_t*>(a.y)[o] = acci[i][j][e];
             else reinterpret_cast<float*>(a.y)[o] = accf[i][j][e];
@@ -457,7 +471,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
             const float sx = a.row_scale ? a.row_scale[m] : a.input_scale;
             const float comb = sx * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
             const float v = T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e];
-            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
+            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(v * comb, a.bias, n);
           }
         }
     }

@@ -190,13 +190,13 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
     if (m >= a.M) break;
     const int64_t o = (int64_t)m * a.N + n;
     if constexpr (SCH == kW8A16) {
-      reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)tot[j];
+      reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(tot[j], a.bias, n);
     } else if (a.out_acc) {
       reinterpret_cast<float*>(a.y)[o] = tot[j];   // int32 bits or fp32
     } else {
       const float v = T::kIntAcc ? (float)__builtin_bit_cast(i32x4, tot)[j] : tot[j];
       const float comb = (a.row_scale ? a.row_scale[m] : a.input_scale) * sw;   // fp32(s_x * s_w[n])
-      reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)(v * comb);
+      reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(v * comb, a.bias, n);
     }
   }
 }

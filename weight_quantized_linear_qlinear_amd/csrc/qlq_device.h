@@ -70,6 +70,18 @@ __device__ __forceinline__ uint32_t f32_to_i8_sat(float v) {
   return (uint32_t)((int)r) & 0xFFu;
 }
 
+// Epilogue bias: fp32(v + b[n]) for a bf16 bias, a separately rounded add (no
+// contraction with the product that formed v).  No bias: v.
+__device__ __forceinline__ float add_bias(float v, const uint16_t* bias, int n) {
+#pragma clang fp contract(off)
+  return bias ? v + bf16_bits_to_f32(bias[n]) : v;
+}
+
+__device__ __forceinline__ float add_bias_value(float v, float b) {
+#pragma clang fp contract(off)
+  return v + b;
+}
+
 // Activation codes: four bf16 (two dwords) -> four codes of sat(RNE(x / s)), an
 // IEEE fp32 division per value (callers must not build with fast-math).
 template <int QT>

@@ -41,6 +41,7 @@ struct GemmArgs {
   int M, K, N, KT, NT;
   float input_scale;
   const float* row_scale;   // W8A8 per-token activation scales [M], or null (static input_scale)
+  const uint16_t* bias;     // bf16 bias [N] added before the bf16 rounding, or null
   int out_acc;
   int fast;                 // K % 64 == 0 and 16-byte aligned rows/pointers
 };
