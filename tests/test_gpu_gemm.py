@@ -219,3 +219,27 @@ def test_split_k_int8_repeated_bit_exact(MKN):
         out.fill_(-1)
         qlq.qlinear_w8a8_static(xq, float(sx), qw, "acc", out=out)
         assert np.array_equal(out.cpu().numpy(), ref), f"rep {rep}"
+
+
+# small-M decode shapes with many column tiles: odd tile counts, ragged N, split-K over long K
+PAIR_SHAPES = [(8, 2048, 8208), (16, 128, 8200), (9, 11008, 8208), (16, 640, 16 * 600)]
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("MKN", PAIR_SHAPES)
+def test_small_m_many_column_tiles(qtype, MKN):
+    M, K, N = MKN
+    print(f"small-M many tiles {qtype} M={M} K={K} N={N}", flush=True)
+    _, calib, x, qw, q_ref, s_ref = _prep(1300 + M + K + N, M, K, N, qtype)
+    y = qlq.qlinear_w8a16(bf16_to_gpu(x), qw)
+    check_close(bits_to_f64(bf16_bits(y)), bits_to_f64(oracle.qlinear_w8a16(x, q_ref, s_ref, qtype)),
+                f"w8a16 many tiles {MKN}")
+    sx = oracle.calibrate_input_scale(calib, qtype)
+    xq_ref = oracle.quantize_act_static(x, sx, qtype)
+    xq = qlq.quantize_act_static(bf16_to_gpu(x), float(sx), qtype)
+    acc = qlq.qlinear_w8a8_static(xq, float(sx), qw, "acc").cpu().numpy()
+    acc_ref = oracle.qlinear_w8a8_static(xq_ref, sx, q_ref, s_ref, qtype, out="acc")
+    if qtype == "int8":
+        assert np.array_equal(acc, acc_ref)
+    else:
+        check_close(acc, acc_ref, f"w8a8 many tiles {MKN}")
