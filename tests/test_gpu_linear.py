@@ -77,3 +77,46 @@ def test_linear_full_size_stack_shapes():
         assert np.array_equal(y, oracle.linear("w8a8_dynamic", x, q_ref, s_ref, "int8", bias_bf16=b))
         y = bf16_bits(qlq.linear("w8a16", bf16_to_gpu(x), qw, bias=bf16_to_gpu(b)))
         check_close(bits_to_f64(y), bits_to_f64(oracle.linear("w8a16", x, q_ref, s_ref, "int8", bias_bf16=b)))
+
+
+def test_graph_replay_of_the_widened_rows():
+    # one HIP graph holding a routed per-token Linear with a bias (a large-M split-K plan and a
+    # small-M split-K plan), a fused static call and a KV-cache round trip; eager calls on the
+    # same workspace run between the replays, and every replay must equal the eager results
+    dev = torch.device("cuda:0")
+    cases = []
+    for i, (M, K, N) in enumerate([(256, 11008, 256), (1, 2048, 2048)]):
+        x, qw, q_ref, s_ref, sx, b = _case(1400 + i, M, K, N, "int8", "w8a8_dynamic")
+        cases.append((bf16_to_gpu(x), qw, bf16_to_gpu(b), float(sx)))
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device=dev)
+    rng = np.random.default_rng(5)
+    kv = [bf16_to_gpu(oracle.f32_to_bf16_bits(rng.standard_normal((64, 4, 128)).astype(np.float32))) for _ in range(2)]
+
+    def work(outs):
+        for (x, qw, b, sx), o in zip(cases, outs[:2]):
+            qlq.linear("w8a8_dynamic", x, qw, bias=b, out=o, workspace=ws)
+        x, qw, b, sx = cases[0]
+        qlq.qlinear_w8a8_static_fused(x, sx, qw, out=outs[2], workspace=ws)
+        q = qlq.kv_quantize(kv[0], kv[1])
+        qlq.kv_dequantize(q, outs[3], outs[4])
+
+    outs = [torch.empty((256, 256), dtype=torch.bfloat16, device=dev), torch.empty((1, 2048), dtype=torch.bfloat16,
+            device=dev), torch.empty((256, 256), dtype=torch.bfloat16, device=dev), torch.empty_like(kv[0]),
+            torch.empty_like(kv[1])]
+    work(outs)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work(outs)
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep}"
+        # eager split-K work on the same workspace between replays
+        x, qw, b, sx = cases[1]
+        qlq.linear("w8a8_dynamic", x, qw, bias=b, workspace=ws)
+        torch.cuda.synchronize()
