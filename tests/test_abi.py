@@ -76,6 +76,10 @@ def test_validation_null_pointers_and_sizes():
     assert st == 1 and ">= 1" in msg
     st, _ = _status(L.qlq_quantize_weight, FAKE, 0, 16, -1, 0, 0, FAKE, FAKE, None)
     assert st == 1
+    # every dimension in range but M * N beyond 2^40 outputs: rejected before any launch
+    big = 1 << 24
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, big, 64, big, FAKE, FAKE, big, 0, FAKE, None, 0, None)
+    assert st == 2 and "2^40" in msg
     st, _ = _status(L.qlq_calibrate_input_scale, FAKE, 0, 0, FAKE, None)
     assert st == 1
 

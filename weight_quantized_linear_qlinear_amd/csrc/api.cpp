@@ -35,6 +35,7 @@ qlq_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;        // keeps every in-kernel index in range
+constexpr int64_t kMaxOutputs = int64_t(1) << 40;   // keeps every launch grid below 2^31
 constexpr int64_t kMaxInt8K = 133144;                // 127 * 127 * K < 2^31
 // Split-K workspaces start with one fixed-size counter region shared by every
 // plan, so partial sums of one call never land on counters of another.
@@ -299,6 +300,7 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
                            const void* bias = nullptr) {
   if (!x || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
   if (qlq_status st = check_dims(M, K, N)) return st;
+  if (M * N > kMaxOutputs) return fail(QLQ_ERR_UNSUPPORTED, "M * N above 2^40 outputs is not supported");
   if (qlq_status st = check_qtype(qtype)) return st;
   if (w_scale_numel != 1 && w_scale_numel != N)
     return fail(QLQ_ERR_INVALID_ARG, "w_scale_numel must be 1 or N (got %lld, N=%lld)", (long long)w_scale_numel,
