@@ -12,8 +12,12 @@
 //    v_mfma_f32_32x32x64_f8f6f4 (W8A8);
 //  * operands move global -> LDS with global_load_lds_dwordx4 (no VGPR staging)
 //    into a ring of NSTAGE stages of 64 inputs each; the loop body is
-//    branch-free and the DMA issues, LDS reads and dequantization are
-//    interleaved between the MFMAs (sched_group_barrier);
+//    branch-free and the DMA issues and LDS reads are interleaved between the
+//    MFMAs (sched_group_barrier);
+//  * W8A16 is software-pipelined by 16-input step: the dequantization and LDS
+//    reads of step q+1 sit between the MFMAs of step q in a fixed order, and
+//    a stage's last step already prepares step 0 of the next stage, so the
+//    stage barrier never leaves the matrix cores waiting on VALU or LDS;
 //  * the bf16 output tile is staged through LDS so global stores are whole
 //    16-byte chunks of rows;
 //  * x rows that fill whole 128-byte lines per stage (bf16 x; 8-bit x with two
@@ -24,8 +28,8 @@
 //    banks; otherwise A fragments land in MFMA lane order.  B is the packed
 //    weight tile copied verbatim (8 whole lines per instruction) and read with
 //    per-lane addresses;
-//  * W8A16 dequantizes B in registers right after the LDS read:
-//    bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
+//  * W8A16 dequantizes B in registers after the LDS read, four codes at a
+//    time: bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
 //  * large per-wave tiles (128 x 64 or 128 x 128) keep LDS traffic within budget.
 //
 // K-slot convention (A and B agree, so the sum over k is unchanged): inside a
@@ -211,31 +215,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     return (r * LINES + (c >> 3)) * 128 + (((c & 7) ^ (l32 & 7)) << 4);
   };
 
+  // W8A8 stage compute (the W8A16 loop has its own pipeline below)
   auto compute = [&](const uint8_t* base) {
 #pragma unroll
     for (int kt = 0; kt < BKT; ++kt) {
-      if constexpr (SCH == kW8A16) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          bf16x8 bfr[TN][2];
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            u32x4 c = lds_read16(base + b_off(wn * TN + j, kt, 2 * p + kg));
-            bfr[j][0] = dequant8<QT>(c.x, c.y, sc[j], sc_m128[j]);
-            bfr[j][1] = dequant8<QT>(c.z, c.w, sc[j], sc_m128[j]);
-          }
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-              bf16x8 af = __builtin_bit_cast(bf16x8, lds_read16(base + a_off(i, kt * 8 + 4 * p + 2 * kg + jj)));
-#pragma unroll
-              for (int j = 0; j < TN; ++j)
-                accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j][jj], af, accf[i][j], 0, 0, 0);
-            }
-          }
-        }
-      } else if constexpr (QT == kInt8) {
+      if constexpr (QT == kInt8) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           i32x4 bfr[TN];
@@ -284,11 +268,107 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     }
   };
 
+  // ---- W8A16 operand helpers for the software-pipelined loop below
+  // DMA instruction idx (0 .. LOADS-1) of stage st_local into ring slot `slot`
+  auto dma_one = [&](int st_local, int slot, int idx) {
+    uint8_t* base = smem + slot * STAGE;
+    if (idx < A_PER_WAVE)
+      dma16(a_src[idx] + (int64_t)st_local * BKT * kTileK * T::kAElem, base + (wave * A_PER_WAVE + idx) * 1024);
+    else
+      dma16(b_src[idx - A_PER_WAVE] + (int64_t)st_local * BKT * kTileBytes,
+            base + (A_FRAGS + wave * B_PER_WAVE + idx - A_PER_WAVE) * 1024);
+  };
+  // 16-input step q of a stage (q = 4 kt + 2 p + jj): A chunk of row block i, and
+  // half h (4 inputs) of the B fragment of column block j from the stage's codes
+  auto a_step = [&](const uint8_t* base, int q, int i) {
+    return lds_read16(base + a_off(i, (q >> 2) * 8 + 4 * ((q >> 1) & 1) + 2 * kg + (q & 1)));
+  };
+  auto read_codes = [&](const uint8_t* base, u32x4 (&bc)[2 * BKT][TN]) {
+#pragma unroll
+    for (int h = 0; h < 2 * BKT; ++h)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bc[h][j] = lds_read16(base + b_off(wn * TN + j, h >> 1, 2 * (h & 1) + kg));
+  };
+  auto b_quarter = [&](const u32x4 (&bc)[2 * BKT][TN], int q, int j, int h) -> u32x2 {
+    const u32x4 c = bc[q >> 1][j];
+    const uint32_t d = (q & 1) ? (h ? c.w : c.z) : (h ? c.y : c.x);
+    return dequant4<QT>(d, sc[j], sc_m128[j]);
+  };
+
   // ---- pipeline: NSTAGE-1 stages in flight ahead of the one being consumed.
   // The loop body is branch-free: the prefetch source is clamped to the last
   // stage, so past the end it re-reads a valid stage into a slot nobody reads,
   // and every iteration waits for the same vmcnt.
-  constexpr int NMFMA = (SCH == kW8A16 ? 4 : (QT == kInt8 ? 2 : 1)) * TM * TN * BKT;
+  if constexpr (SCH == kW8A16) {
+    // W8A16: the dequantization (VALU) and LDS reads of step q+1 run between
+    // the MFMAs of step q, in a fixed order (sched_barrier after each MFMA).
+    // The stage barrier sits before a stage's last step: that step needs no
+    // LDS of its own stage (its operands are already in registers), so it
+    // reads and dequantizes step 0 of the next stage.  Slot (t-1) is last
+    // read before that barrier, so stage t's DMA issues (spread over its
+    // first MFMAs) may overwrite it.
+    constexpr int Q = 4 * BKT, NM = TM * TN;
+    static_assert(TM >= 2 && (Q - 1) * NM >= LOADS, "W8A16 pipeline shape");
+    u32x4 bc[2 * BKT][TN];
+    u32x4 af[2][TM];
+    u32x2 bq[2][TN][2];
+#pragma unroll
+    for (int t = 0; t < NSTAGE - 1; ++t) issue(t < nst ? t : nst - 1, t);
+    wait_vmcnt<LOADS * (NSTAGE - 2)>();
+    __syncthreads();
+    read_codes(smem, bc);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = a_step(smem, 0, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      bq[0][j][0] = b_quarter(bc, 0, j, 0);
+      bq[0][j][1] = b_quarter(bc, 0, j, 1);
+    }
+    for (int t = 0; t < nst; ++t) {
+      const uint8_t* cur = smem + (t % NSTAGE) * STAGE;
+      const uint8_t* nxt = smem + ((t + 1) % NSTAGE) * STAGE;   // past the end: a valid slot, unused
+      const int pf = t + NSTAGE - 1 < nst ? t + NSTAGE - 1 : nst - 1;
+      const int pslot = (t + NSTAGE - 1) % NSTAGE;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int c = q & 1;
+        if (q == Q - 1) {
+          // Stage t+1 visible, slot t-1 free.  This wave's DMAs of stage t+1
+          // are complete (vmcnt), and its reads of slot t-1 were consumed long
+          // ago, so no release fence: one would wait for the stage t+2 DMAs too.
+          wait_vmcnt<LOADS * (NSTAGE - 2)>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const int i = m / TN, j = m % TN;
+          const u32x4 bv = (u32x4){bq[c][j][0].x, bq[c][j][0].y, bq[c][j][1].x, bq[c][j][1].y};
+          accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bv),
+                                                                __builtin_bit_cast(bf16x8, af[c][i]), accf[i][j], 0, 0, 0);
+          if (q * NM + m < LOADS) dma_one(pf, pslot, q * NM + m);
+          if (q + 1 < Q) {
+#pragma unroll
+            for (int pc = 0; pc < 2 * TN; ++pc)
+              if (m == pc * NM / (2 * TN)) bq[c ^ 1][pc >> 1][pc & 1] = b_quarter(bc, q + 1, pc >> 1, pc & 1);
+            if (m % TN == TN - 1) af[c ^ 1][m / TN] = a_step(cur, q + 1, m / TN);
+          } else {
+            if (m == 0) read_codes(nxt, bc);
+            if (m == 1) {
+#pragma unroll
+              for (int ii = 0; ii < TM; ++ii) af[c ^ 1][ii] = a_step(nxt, 0, ii);
+            }
+#pragma unroll
+            for (int pc = 0; pc < 2 * TN; ++pc)
+              if (m == 2 + pc * (NM - 2) / (2 * TN)) bq[c ^ 1][pc >> 1][pc & 1] = b_quarter(bc, 0, pc >> 1, pc & 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else {
+  constexpr int NMFMA = (QT == kInt8 ? 2 : 1) * TM * TN * BKT;
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t) issue(t < nst ? t : nst - 1, t);
   for (int t = 0; t < nst; ++t) {
@@ -303,8 +383,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
       if (i < LOADS) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // VMEM (DMA)
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      // DS read
-      if (SCH == kW8A16) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU (dequant)
     }
+  }
   }
   wait_vmcnt<0>();                                           // no DMA may outlive the loop
 
