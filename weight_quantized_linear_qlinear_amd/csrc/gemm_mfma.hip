@@ -103,7 +103,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
   static_assert(LINE_A || SCH == kW8A8, "bf16 x always fills whole lines");
   constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;             // DMA instructions per wave per stage
   static_assert(A_FRAGS % NW == 0 && B_TILES % NW == 0, "DMA split");
-  static_assert(LOADS * (NSTAGE - 2) < 64, "vmcnt range");
+  static_assert(LOADS * (NSTAGE - 1) < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -215,59 +215,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     return (r * LINES + (c >> 3)) * 128 + (((c & 7) ^ (l32 & 7)) << 4);
   };
 
-  // W8A8 stage compute (the W8A16 loop has its own pipeline below)
-  auto compute = [&](const uint8_t* base) {
-#pragma unroll
-    for (int kt = 0; kt < BKT; ++kt) {
-      if constexpr (QT == kInt8) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          i32x4 bfr[TN];
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            bfr[j] = __builtin_bit_cast(i32x4, lds_read16(base + b_off(wn * TN + j, kt, 2 * p + kg)));
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            i32x4 af;
-            if constexpr (LINE_A) {
-              af = __builtin_bit_cast(i32x4, lds_read16(base + a_off(i, kt * 4 + 2 * p + kg)));
-            } else {
-              const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + p;
-              af = __builtin_bit_cast(i32x4, lds_read16(base + f * 1024 + lane * 16));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfr[j], af, acci[i][j], 0, 0, 0);
-          }
-        }
-      } else {
-        i32x8 bfr[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          u32x4 c0 = lds_read16(base + b_off(wn * TN + j, kt, 2 * kg));
-          u32x4 c1 = lds_read16(base + b_off(wn * TN + j, kt, 2 * kg + 1));
-          bfr[j] = (i32x8){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          u32x4 a0, a1;
-          if constexpr (LINE_A) {
-            a0 = lds_read16(base + a_off(i, kt * 4 + 2 * kg));
-            a1 = lds_read16(base + a_off(i, kt * 4 + 2 * kg + 1));
-          } else {
-            const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags;
-            a0 = lds_read16(base + f * 1024 + lane * 16);
-            a1 = lds_read16(base + (f + 1) * 1024 + lane * 16);
-          }
-          i32x8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af, accf[i][j], 0, 0, 0, 0, 0, 0);
-        }
-      }
-    }
-  };
-
   // ---- W8A16 operand helpers for the software-pipelined loop below
   // DMA instruction idx (0 .. LOADS-1) of stage st_local into ring slot `slot`
   auto dma_one = [&](int st_local, int slot, int idx) {
@@ -304,17 +251,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     // the MFMAs of step q, in a fixed order (sched_barrier after each MFMA).
     // The stage barrier sits before a stage's last step: that step needs no
     // LDS of its own stage (its operands are already in registers), so it
-    // reads and dequantizes step 0 of the next stage.  Slot (t-1) is last
-    // read before that barrier, so stage t's DMA issues (spread over its
-    // first MFMAs) may overwrite it.
-    constexpr int Q = 4 * BKT, NM = TM * TN;
-    static_assert(TM >= 2 && (Q - 1) * NM >= LOADS, "W8A16 pipeline shape");
+    // reads and dequantizes step 0 of the next stage, and it issues the DMAs
+    // of stage t + NSTAGE into the slot of stage t, whose last reader passed
+    // the barrier.  Each stage's DMAs get NSTAGE - 1 whole stages to land.
+    constexpr int Q = 4 * BKT, NM = TM * TN, DPM = (LOADS + NM - 1) / NM;
+    static_assert(TM >= 2, "W8A16 pipeline shape");
     u32x4 bc[2 * BKT][TN];
     u32x4 af[2][TM];
     u32x2 bq[2][TN][2];
 #pragma unroll
-    for (int t = 0; t < NSTAGE - 1; ++t) issue(t < nst ? t : nst - 1, t);
-    wait_vmcnt<LOADS * (NSTAGE - 2)>();
+    for (int t = 0; t < NSTAGE; ++t) issue(t < nst ? t : nst - 1, t);
+    wait_vmcnt<LOADS * (NSTAGE - 1)>();
     __syncthreads();
     read_codes(smem, bc);
 #pragma unroll
@@ -327,16 +274,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     for (int t = 0; t < nst; ++t) {
       const uint8_t* cur = smem + (t % NSTAGE) * STAGE;
       const uint8_t* nxt = smem + ((t + 1) % NSTAGE) * STAGE;   // past the end: a valid slot, unused
-      const int pf = t + NSTAGE - 1 < nst ? t + NSTAGE - 1 : nst - 1;
-      const int pslot = (t + NSTAGE - 1) % NSTAGE;
+      const int pf = t + NSTAGE < nst ? t + NSTAGE : nst - 1;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int c = q & 1;
         if (q == Q - 1) {
-          // Stage t+1 visible, slot t-1 free.  This wave's DMAs of stage t+1
-          // are complete (vmcnt), and its reads of slot t-1 were consumed long
-          // ago, so no release fence: one would wait for the stage t+2 DMAs too.
+          // Stage t+1 visible, slot t free.  This wave's DMAs of stage t+1 are
+          // complete (vmcnt) and its reads of slot t were consumed, so no
+          // release fence: one would also wait for the younger stages' DMAs.
           wait_vmcnt<LOADS * (NSTAGE - 2)>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -347,13 +293,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
           const u32x4 bv = (u32x4){bq[c][j][0].x, bq[c][j][0].y, bq[c][j][1].x, bq[c][j][1].y};
           accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bv),
                                                                 __builtin_bit_cast(bf16x8, af[c][i]), accf[i][j], 0, 0, 0);
-          if (q * NM + m < LOADS) dma_one(pf, pslot, q * NM + m);
           if (q + 1 < Q) {
 #pragma unroll
             for (int pc = 0; pc < 2 * TN; ++pc)
               if (m == pc * NM / (2 * TN)) bq[c ^ 1][pc >> 1][pc & 1] = b_quarter(bc, q + 1, pc >> 1, pc & 1);
             if (m % TN == TN - 1) af[c ^ 1][m / TN] = a_step(cur, q + 1, m / TN);
           } else {
+#pragma unroll
+            for (int d = 0; d < DPM; ++d)
+              if (m * DPM + d < LOADS) dma_one(pf, t % NSTAGE, m * DPM + d);
             if (m == 0) read_codes(nxt, bc);
             if (m == 1) {
 #pragma unroll
@@ -368,23 +316,90 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
       }
     }
   } else {
-  constexpr int NMFMA = (QT == kInt8 ? 2 : 1) * TM * TN * BKT;
+    // W8A8: the same pipeline without dequantization.  A step is one MFMA
+    // deep in K: 32 inputs (int8) or 64 (fp8, two 16-byte reads per operand).
+    constexpr int Q = QT == kInt8 ? 2 * BKT : BKT, NM = TM * TN, NR = QT == kInt8 ? 1 : 2;
+    constexpr int DPM = (LOADS + NM - 1) / NM;
+    // operands of step q (int8: q = 2 kt + p, chunk 2p + kg; fp8: q = kt, chunks 2kg and 2kg + 1)
+    auto read_a = [&](const uint8_t* base, int q, int i, u32x4 (&dst)[NR]) {
 #pragma unroll
-  for (int t = 0; t < NSTAGE - 1; ++t) issue(t < nst ? t : nst - 1, t);
-  for (int t = 0; t < nst; ++t) {
-    wait_vmcnt<LOADS * (NSTAGE - 2)>();
-    __syncthreads();                                         // stage t visible; slot (t-1) free
-    const int pf = t + NSTAGE - 1 < nst ? t + NSTAGE - 1 : nst - 1;
-    issue(pf, (t + NSTAGE - 1) % NSTAGE);
-    compute(smem + (t % NSTAGE) * STAGE);
-    // interleave: spread the DMA issues and LDS reads between the MFMAs
+      for (int r = 0; r < NR; ++r) {
+        const int kt = QT == kInt8 ? q >> 1 : q;
+        if constexpr (LINE_A) {
+          dst[r] = lds_read16(base + a_off(i, QT == kInt8 ? kt * 4 + 2 * (q & 1) + kg : kt * 4 + 2 * kg + r));
+        } else {
+          const int f = ((wm * TM + i) * BKT + kt) * T::kAFrags + (QT == kInt8 ? (q & 1) : r);
+          dst[r] = lds_read16(base + f * 1024 + lane * 16);
+        }
+      }
+    };
+    auto read_b = [&](const uint8_t* base, int q, int j, u32x4 (&dst)[NR]) {
 #pragma unroll
-    for (int i = 0; i < NMFMA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-      if (i < LOADS) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // VMEM (DMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                      // DS read
+      for (int r = 0; r < NR; ++r)
+        dst[r] = QT == kInt8 ? lds_read16(base + b_off(wn * TN + j, q >> 1, 2 * (q & 1) + kg))
+                             : lds_read16(base + b_off(wn * TN + j, q, 2 * kg + r));
+    };
+    auto mma = [&](const u32x4 (&b)[NR], const u32x4 (&a)[NR], int i, int j) {
+      if constexpr (QT == kInt8) {
+        acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, a[0]),
+                                                           acci[i][j], 0, 0, 0);
+      } else {
+        const i32x8 bb = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w, (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+        const i32x8 aa = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w, (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+        accf[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, accf[i][j], 0, 0, 0, 0, 0, 0);
+      }
+    };
+    u32x4 af[2][TM][NR], bf[2][TN][NR];
+#pragma unroll
+    for (int t = 0; t < NSTAGE; ++t) issue(t < nst ? t : nst - 1, t);
+    wait_vmcnt<LOADS * (NSTAGE - 1)>();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TN; ++j) read_b(smem, 0, j, bf[0][j]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_a(smem, 0, i, af[0][i]);
+    for (int t = 0; t < nst; ++t) {
+      const uint8_t* cur = smem + (t % NSTAGE) * STAGE;
+      const uint8_t* nxt = smem + ((t + 1) % NSTAGE) * STAGE;   // past the end: a valid slot, unused
+      const int pf = t + NSTAGE < nst ? t + NSTAGE : nst - 1;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int c = q & 1;
+        const uint8_t* src = q + 1 < Q ? cur : nxt;            // operands of the following step
+        const int qn = q + 1 < Q ? q + 1 : 0;
+        if (q == Q - 1) {                                      // as in the W8A16 loop
+          wait_vmcnt<LOADS * (NSTAGE - 2)>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mma(bf[c][m % TN], af[c][m / TN], m / TN, m % TN);
+          if (q == Q - 1) {
+#pragma unroll
+            for (int d = 0; d < DPM; ++d)
+              if (m * DPM + d < LOADS) dma_one(pf, t % NSTAGE, m * DPM + d);
+          }
+          if (m == 0) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) read_b(src, qn, j, bf[c ^ 1][j]);
+          }
+          if (m % TN == TN - 1) read_a(src, qn, m / TN, af[c ^ 1][m / TN]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (Q & 1) {                                   // step 0 of the next stage landed in buffer 1
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) af[0][i][r] = af[1][i][r];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) bf[0][j][r] = bf[1][j][r];
+      }
     }
-  }
   }
   wait_vmcnt<0>();                                           // no DMA may outlive the loop
 
