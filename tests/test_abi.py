@@ -58,7 +58,8 @@ def test_packed_bytes_is_tile_padded_and_about_half_of_bf16():
 
 def test_workspace_sizes():
     assert qlq.workspace_bytes("w8a16", 16, 2048, 11008, "fp8_e4m3fn") == 0      # enough column blocks
-    assert qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8") > 0               # split over K
+    assert qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8") == 0              # waves split K in one workgroup
+    assert qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8") > 0               # narrow N: split over K
     assert qlq.workspace_bytes("w8a8_static", 1024, 2048, 11008, "fp8_e4m3fn") == 0
     assert qlq.workspace_bytes("w8a8_static", 256, 11008, 2048, "int8") > 0
     assert qlq.workspace_bytes("w8a16", 0, 64, 64, "int8") == 0
@@ -103,10 +104,10 @@ def test_validation_enums_scales_and_workspace():
     st, msg = _status(L.qlq_qlinear_w8a8_static, FAKE, 1.0, 4, 133145, 16, FAKE, FAKE, 16, 0, 0, FAKE, None, 0, None)
     assert st == 1 and "133144" in msg
     # a split-K plan needs its workspace
-    need = qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8")
-    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 2048, FAKE, FAKE, 2048, 0, FAKE, None, 0, None)
+    need = qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8")
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 1024, FAKE, FAKE, 1024, 0, FAKE, None, 0, None)
     assert st == 1 and "workspace" in msg
-    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 2048, FAKE, FAKE, 2048, 0, FAKE, FAKE, need - 1, None)
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 1024, FAKE, FAKE, 1024, 0, FAKE, FAKE, need - 1, None)
     assert st == 1 and "workspace" in msg
     # misaligned packed weights
     st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 64, 16, ctypes.c_void_p(0x10008), FAKE, 16, 0, FAKE, None, 0,

@@ -2,6 +2,7 @@
 // Declarations and their contracts: include/qlq.h.
 #include "qlq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -133,29 +134,33 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
   GemmPlan p;
   const int64_t KT = cdiv(K, 64), NT = cdiv(N, 16);
   if (M <= 16) {
-    // Small-M: one workgroup per 16 output columns and K slice; enough
-    // workgroups to cover the 256 CUs about twice.
+    // Small-M: one workgroup per 16 output columns, with 4, 8 or 16 waves
+    // splitting K inside it (summed through LDS).  Measured on MI355X over
+    // decode shapes with N from 2048 to 14336 and K from 2048 to 14336: K splits
+    // across workgroups cost more than they gain (the partial-sum handoff is a
+    // few memory round trips) except for narrow, deep weights, and each wave
+    // should issue all its loads at once (at most kSmallUnitsPerWave units),
+    // with about 2048 waves or more in the grid.  FP8 W8A8 stops at 8 waves
+    // (its 16-wave build would spill registers).
     p.kind = 0;
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
     const int64_t KU = cdiv(KT, TPU);
-    // Each wave handles at most kSmallUnitsPerWave K units (all its loads go out
-    // before the first wait); small column counts are also split to fill the GPU.
-    int64_t S = cdiv(KU, 4 * kSmallUnitsPerWave);
-    if (NT < 512) {   // NT < 512 <= kMaxSplitTiles
-      int64_t want = cdiv(512, NT);
-      int64_t cap = KU / 4 > 1 ? KU / 4 : 1;
-      if (want > cap) want = cap;
-      if (want > S) S = want;
-    }
-    if (S > 1 && NT > kMaxSplitTiles) S = 1;   // cannot happen for K < 2^24 with the bound above
+    const int64_t max_waves = TPU == 2 ? 8 : 16;
+    int64_t S = 1;
+    if (NT < 128) S = std::min(cdiv(128, NT), std::max<int64_t>(1, KU / kSmallUnitsPerWave));
+    else if (NT < 192 && KU >= 96) S = 2;
     const int64_t ups = cdiv(KU, S);
     S = cdiv(KU, ups);
+    int64_t W = 4;
+    while (W < max_waves && cdiv(ups, W) > kSmallUnitsPerWave) W *= 2;
+    while (W < max_waves && NT * S * W <= 2048) W *= 2;
     p.S = (int)S;
     p.units_per_split = (int)ups;
-    p.units_per_wave = (int)cdiv(ups, 4);
+    p.units_per_wave = (int)cdiv(ups, W);
+    p.waves = (int)W;
     p.tiles = (int)NT;
     p.grid = (int)(NT * S);
-    if (S > 1) {
+    if (S > 1) {   // S > 1 only when NT < 192 <= kMaxSplitTiles
       p.ws_counter_bytes = kCounterBytes;
       p.ws_bytes = p.ws_counter_bytes + (size_t)S * NT * 64 * 16;
     }

@@ -13,8 +13,8 @@
 // M <= 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
 //
 // Work split: workgroup (nt, s) owns output columns [16 nt, 16 nt + 16) and the
-// s-th slice of K; its four waves take consecutive sub-slices.  The four wave
-// accumulators are summed through LDS; with S > 1 slices per column block the
+// s-th slice of K; its NW (4, 8 or 16) waves take consecutive sub-slices.  The
+// wave accumulators are summed through LDS; with S > 1 slices per column block the
 // partial sums go to the workspace and the last workgroup to arrive adds them
 // in slice order (deterministic) and runs the epilogue.  The handoff uses
 // agent-coherent partial stores and a device atomic counter (qlq_device.h).
@@ -25,7 +25,6 @@ namespace qlq {
 
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kUnroll = 8;
 
 template <int QT, int SCH>
@@ -71,8 +70,8 @@ __device__ __forceinline__ u32x4 load_x_codes16(const uint8_t* row, int k, int K
   }
 }
 
-template <int QT, int SCH, bool FAST>
-__global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int ups, int upw) {
+template <int QT, int SCH, bool FAST, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, int ups, int upw) {
   using T = SmallTraits<QT, SCH>;
   constexpr int TPU = T::kTilesPerUnit;
   constexpr int kU = kUnroll;
@@ -141,8 +140,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
     }
   }
 
-  // ---- sum the four waves through LDS (wave 0 finishes the job)
-  __shared__ f32x4 red[kWaves][64];
+  // ---- sum the waves through LDS (wave 0 finishes the job)
+  __shared__ f32x4 red[NW][64];
   f32x4 mine = T::kIntAcc ? __builtin_bit_cast(f32x4, acci) : accf;
   red[wave][lane] = mine;
   __syncthreads();
@@ -150,11 +149,11 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
   f32x4 tot;
   if constexpr (T::kIntAcc) {
     i32x4 t = __builtin_bit_cast(i32x4, red[0][lane]);
-    for (int w = 1; w < kWaves; ++w) t += __builtin_bit_cast(i32x4, red[w][lane]);
+    for (int w = 1; w < NW; ++w) t += __builtin_bit_cast(i32x4, red[w][lane]);
     tot = __builtin_bit_cast(f32x4, t);
   } else {
     tot = red[0][lane];
-    for (int w = 1; w < kWaves; ++w) tot += red[w][lane];
+    for (int w = 1; w < NW; ++w) tot += red[w][lane];
   }
 
   // ---- split-K: publish, count arrivals, last one sums the slices in order
@@ -201,13 +200,23 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a, int S, int 
   }
 }
 
+template <int QT, int SCH, int NW>
+hipError_t launch_small_w(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  if (a.fast)
+    gemm_small_kernel<QT, SCH, true, NW><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  else
+    gemm_small_kernel<QT, SCH, false, NW><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  return hipGetLastError();
+}
+
 template <int QT, int SCH>
 hipError_t launch_small_t(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-  if (a.fast)
-    gemm_small_kernel<QT, SCH, true><<<p.grid, 256, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
-  else
-    gemm_small_kernel<QT, SCH, false><<<p.grid, 256, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
-  return hipGetLastError();
+  switch (p.waves) {
+    case 4: return launch_small_w<QT, SCH, 4>(p, a, st);
+    case 8: return launch_small_w<QT, SCH, 8>(p, a, st);
+    case 16: return launch_small_w<QT, SCH, 16>(p, a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
