@@ -148,7 +148,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     const int64_t max_waves = TPU == 2 ? 8 : 16;
     int64_t S = 1;
     if (NT < 128) S = std::min(cdiv(128, NT), std::max<int64_t>(1, KU / kSmallUnitsPerWave));
-    else if (NT < 192 && KU >= 96) S = 2;
+    else if (NT < 192 && KU >= 64) S = 2;
     const int64_t ups = cdiv(KU, S);
     S = cdiv(KU, ups);
     int64_t W = 4;
