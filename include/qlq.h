@@ -165,6 +165,27 @@ qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale,
                                    void* y, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* W8A8 static with the next layer's static activation quantization in the
+ * epilogue.  y is exactly what qlq_qlinear_w8a8_static writes with QLQ_OUT_BF16,
+ * and in the same pass
+ *   y_codes[m,n] = sat(round-to-nearest-even(fp32(y[m,n]) / next_scale))
+ * (the bf16 value rounded first), i.e. the codes qlq_quantize_act_static(y,
+ * next_scale, qtype) would write.  It serves a chain of projections whose next
+ * layer is a static W8A8 layer with input scale next_scale (the key-design list
+ * of the INT8 section of the "Nano-vLLM-MOE" mirror: one fixed scalar per layer,
+ * no reduction at run time), so the next layer's quantization costs no extra
+ * pass over y.  y bf16 [M, N]; y_codes [M, N] one byte per code, 16-byte
+ * aligned.  The workspace is the one of qlq_qlinear_w8a8_static (size it with
+ * QLQ_SCHEME_W8A8_STATIC).  Errors: those of qlq_qlinear_w8a8_static, plus a
+ * non-finite or <= 0 next_scale and a null or misaligned y_codes
+ * (QLQ_ERR_INVALID_ARG). */
+qlq_status qlq_qlinear_w8a8_static_requant(const void* xq, float input_scale,
+                                           int64_t M, int64_t K, int64_t N,
+                                           const void* wq_packed, const float* w_scale,
+                                           int64_t w_scale_numel, qlq_qtype qtype, float next_scale,
+                                           void* y, void* y_codes, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
 /* W8A8 static from bf16 activations: the same result as qlq_quantize_act_static
  * followed by qlq_qlinear_w8a8_static (identical codes, accumulators and
  * outputs), as one call.  The codes go through the workspace: one quantization

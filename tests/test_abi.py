@@ -207,3 +207,21 @@ def test_routed_linear_workspace_sizes():
         d = qlq.linear_workspace_bytes("w8a8_dynamic", M, K, N, "int8")
         assert s >= qlq.workspace_bytes("w8a8_static", M, K, N, "int8") + M * K and d >= s + 4 * M
         assert s >= qlq.workspace_bytes("w8a16", M, K, N, "int8")          # the fallback fits too
+
+
+def test_validation_of_the_requant_call():
+    L = qlq.lib()
+    f = L.qlq_qlinear_w8a8_static_requant
+    for bad in [0.0, -2.0, float("inf"), float("nan")]:
+        st, msg = _status(f, FAKE, 1.0, 4, 64, 16, FAKE, FAKE, 16, 0, bad, FAKE, FAKE, None, 0, None)
+        assert st == 1 and "next_scale" in msg
+        st, msg = _status(f, FAKE, bad, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, FAKE, FAKE, None, 0, None)
+        assert st == 1 and "input_scale" in msg
+    st, msg = _status(f, FAKE, 1.0, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, FAKE, None, None, 0, None)
+    assert st == 1 and "null" in msg
+    st, msg = _status(f, FAKE, 1.0, 4, 64, 16, FAKE, FAKE, 16, 0, 1.0, FAKE, ctypes.c_void_p(0x10008), None, 0, None)
+    assert st == 1 and "aligned" in msg
+    st, msg = _status(f, FAKE, 1.0, 4, 133145, 16, FAKE, FAKE, 16, 0, 1.0, FAKE, FAKE, None, 0, None)
+    assert st == 1 and "133144" in msg
+    st, _ = _status(f, FAKE, 1.0, 4, 64, 16, FAKE, FAKE, 16, 5, 1.0, FAKE, FAKE, None, 0, None)
+    assert st == 2

@@ -6,6 +6,7 @@ include/qlq.h); this package is its Python binding.
 from .binding import (QTYPES, GRANULARITIES, QlqError, QuantizedKV, QuantizedWeight, calibrate_input_scale,
                       code_dtype, kv_dequantize, kv_quantize, lib, library_path, linear, linear_workspace_bytes, packed_weight_bytes, qlinear_w8a16,
                       qlinear_w8a8_dynamic, qlinear_w8a8_static, qlinear_w8a8_static_fused,
+                      qlinear_w8a8_static_requant,
                       quantize_act_dynamic, quantize_act_static, quantize_weight, unpack_weight,
                       workspace_bytes)
 
@@ -13,6 +14,7 @@ __all__ = [
     "QTYPES", "GRANULARITIES", "QlqError", "QuantizedKV", "QuantizedWeight", "calibrate_input_scale", "code_dtype",
     "kv_dequantize", "kv_quantize", "linear", "linear_workspace_bytes",
     "lib", "library_path", "packed_weight_bytes", "qlinear_w8a16", "qlinear_w8a8_dynamic",
-    "qlinear_w8a8_static", "qlinear_w8a8_static_fused", "quantize_act_dynamic", "quantize_act_static",
+    "qlinear_w8a8_static", "qlinear_w8a8_static_fused", "qlinear_w8a8_static_requant", "quantize_act_dynamic",
+    "quantize_act_static",
     "quantize_weight", "unpack_weight", "workspace_bytes",
 ]

@@ -39,6 +39,10 @@ _SIGNATURES = {
     "qlq_qlinear_w8a8_static": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
                                            _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
                                            _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_qlinear_w8a8_static_requant": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                   _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_float,
+                                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                                   _c.c_void_p]),
     "qlq_quantize_act_dynamic": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
                                             _c.c_void_p, _c.c_void_p]),
     "qlq_qlinear_w8a8_static_fused": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
@@ -268,6 +272,30 @@ def qlinear_w8a8_static(xq: torch.Tensor, input_scale: float, qw: QuantizedWeigh
                                          _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
                                          _stream(xq.device)))
     return out
+
+
+def qlinear_w8a8_static_requant(xq: torch.Tensor, input_scale: float, qw: QuantizedWeight, next_scale: float,
+                                out: torch.Tensor | None = None, out_codes: torch.Tensor | None = None,
+                                workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """W8A8 static GEMM on codes xq [M, K] that also quantizes its bf16 output for the next static layer:
+    returns (y bf16 [M, N], codes [M, N] of y at next_scale, same qtype)."""
+    _require_gpu(xq)
+    if xq.dim() != 2 or xq.element_size() != 1 or xq.shape[1] != qw.K:
+        raise ValueError(f"xq must be 1-byte codes [M, {qw.K}]")
+    M = xq.shape[0]
+    if out is None:
+        out = torch.empty((M, qw.N), dtype=torch.bfloat16, device=xq.device)
+    if out_codes is None:
+        out_codes = torch.empty((M, qw.N), dtype=code_dtype(qw.qtype), device=xq.device)
+    if out_codes.shape != (M, qw.N) or out_codes.element_size() != 1:
+        raise ValueError(f"out_codes must be 1-byte codes [{M}, {qw.N}]")
+    nbytes = workspace_bytes("w8a8_static", M, qw.K, qw.N, qw.qtype)
+    ws = workspace if workspace is not None else _workspace(xq.device, nbytes)
+    _check(lib().qlq_qlinear_w8a8_static_requant(_ptr(xq), float(input_scale), M, qw.K, qw.N, _ptr(qw.packed),
+                                                 _ptr(qw.scale), qw.scale.numel(), _qtype(qw.qtype),
+                                                 float(next_scale), _ptr(out), _ptr(out_codes), _ptr(ws),
+                                                 0 if ws is None else ws.numel(), _stream(xq.device)))
+    return out, out_codes
 
 
 def _w8a8_out(M: int, qw: QuantizedWeight, out_mode: str, dev: torch.device) -> torch.Tensor:

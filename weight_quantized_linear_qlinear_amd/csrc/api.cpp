@@ -303,7 +303,7 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
                            const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
                            const float* row_scale, int out_acc, void* y, void* workspace,
                            size_t workspace_bytes, hipStream_t stream, const char* what,
-                           const void* bias = nullptr) {
+                           const void* bias = nullptr, void* y_codes = nullptr, float next_scale = 1.0f) {
   if (!x || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
   if (qlq_status st = check_dims(M, K, N)) return st;
   if (M * N > kMaxOutputs) return fail(QLQ_ERR_UNSUPPORTED, "M * N above 2^40 outputs is not supported");
@@ -343,6 +343,8 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.input_scale = input_scale;
   a.row_scale = row_scale;
   a.bias = static_cast<const uint16_t*>(bias);
+  a.y_codes = static_cast<uint8_t*>(y_codes);
+  a.next_scale = next_scale;
   a.out_acc = out_acc;
   a.fast = fast;
   hipError_t e = plan.kind == 0   ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
@@ -369,6 +371,21 @@ qlq_status qlq_qlinear_w8a8_static(const void* xq, float input_scale, int64_t M,
                 (long long)kMaxInt8K);
   return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale, nullptr,
                   out == QLQ_OUT_ACC ? 1 : 0, y, workspace, workspace_bytes, stream, "qlinear_w8a8_static");
+}
+
+qlq_status qlq_qlinear_w8a8_static_requant(const void* xq, float input_scale, int64_t M, int64_t K, int64_t N,
+                                           const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                                           qlq_qtype qtype, float next_scale, void* y, void* y_codes,
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (qlq_status st = check_scale(input_scale, "input_scale")) return st;
+  if (qlq_status st = check_scale(next_scale, "next_scale")) return st;
+  if (!y_codes) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(y_codes, 16)) return fail(QLQ_ERR_INVALID_ARG, "y_codes must be 16-byte aligned");
+  if (qtype == QLQ_INT8 && K > kMaxInt8K)
+    return fail(QLQ_ERR_INVALID_ARG, "INT8 W8A8 needs K <= %lld for an exact int32 accumulator",
+                (long long)kMaxInt8K);
+  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale, nullptr, 0, y,
+                  workspace, workspace_bytes, stream, "qlinear_w8a8_static_requant", nullptr, y_codes, next_scale);
 }
 
 static qlq_status check_w8a8(qlq_qtype qtype, qlq_out out, int64_t K) {

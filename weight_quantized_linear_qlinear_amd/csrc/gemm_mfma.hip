@@ -543,6 +543,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
           const __bf16* src = reinterpret_cast<const __bf16*>(&v);
           for (int e = 0; e < a.N - n; ++e) dst[e] = src[e];
         }
+        if (SCH == kW8A8 && a.y_codes) {                     // next layer's codes of these 8 outputs
+          const u32x2 q = {quant4<QT>(v.x, v.y, a.next_scale), quant4<QT>(v.z, v.w, a.next_scale)};
+          uint8_t* cdst = a.y_codes + (int64_t)m * a.N + n;
+          if (n + 8 <= a.N) {
+            *reinterpret_cast<u32x2*>(cdst) = q;
+          } else {
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(&q);
+            for (int e = 0; e < a.N - n; ++e) cdst[e] = src[e];
+          }
+        }
       }
     }
   } else {
@@ -566,7 +576,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
             const float sx = a.row_scale ? a.row_scale[m] : a.input_scale;
             const float comb = sx * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
             const float v = T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e];
-            reinterpret_cast<__bf16*>(a.y)[o] = (__bf16)add_bias(v * comb, a.bias, n);
+            store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale);
           }
         }
     }

@@ -92,6 +92,23 @@ __device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s) {
   return f32_to_i8_sat(a) | (f32_to_i8_sat(b) << 8) | (f32_to_i8_sat(c) << 16) | (f32_to_i8_sat(d) << 24);
 }
 
+// One bf16 (bits) -> its activation code sat(RNE(x / s)), as quant4.
+template <int QT>
+__device__ __forceinline__ uint32_t quant1(uint32_t b, float s) {
+  const float v = bf16_bits_to_f32(b) / s;
+  if constexpr (QT == kFp8) return f32x4_to_e4m3x4_sat(v, 0.0f, 0.0f, 0.0f) & 0xFFu;
+  return f32_to_i8_sat(v);
+}
+
+// bf16 output element y[o] = bf16(val) and, with a code buffer, codes[o] = the
+// activation code of that bf16 value at scale s (requantization for the next layer).
+template <int QT>
+__device__ __forceinline__ void store_bf16_requant(void* y, uint8_t* codes, int64_t o, float val, float s) {
+  const __bf16 h = (__bf16)val;
+  reinterpret_cast<__bf16*>(y)[o] = h;
+  if (codes) codes[o] = (uint8_t)quant1<QT>(__builtin_bit_cast(uint16_t, h), s);
+}
+
 // Dequantize 8 codes (two dwords) to 8 bf16 = bf16(fp32(q) * s), one fp32
 // rounding for the product and one for the bf16 cast.
 template <int QT>

@@ -43,6 +43,8 @@ struct GemmArgs {
   float input_scale;
   const float* row_scale;   // W8A8 per-token activation scales [M], or null (static input_scale)
   const uint16_t* bias;     // bf16 bias [N] added before the bf16 rounding, or null
+  uint8_t* y_codes;         // W8A8: codes [M,N] of the bf16 output at next_scale (the next
+  float next_scale;         //   layer's static activation quantization), or null
   int out_acc;
   int fast;                 // K % 64 == 0 and 16-byte aligned rows/pointers
 };
