@@ -11,9 +11,11 @@ quantization"):
     * FP8 W8A8 static (per-tensor weight scale, per-layer input scales
       calibrated offline on a 64-row batch through the bf16-dequant chain),
   swept over M in {1, 16, 256, 1024}.
-One step = the 8 chains (2 variants x 4 M) = 864 GEMMs.  The FP8 W8A8 chain
-calls the fused static entry point (activation codes made inside the GEMM at
-M <= 16, one quantization pass before it above).  Each chain is captured once
+One step = the 8 chains (2 variants x 4 M) = 864 GEMMs.  In the FP8 W8A8 chain
+each layer's epilogue writes, beside its bf16 output, that output's codes at the
+next layer's static input scale (qlq_qlinear_w8a8_static_requant), so the only
+separate activation quantization is the one of the chain's input; the last layer
+writes no codes.  Each chain is captured once
 as a HIP graph and replayed, so the timed region holds GPU work only; weights
 (1.65 GiB per variant) are far larger than the 256 MB last-level cache, so
 every step streams them from HBM.
@@ -52,7 +54,7 @@ METRIC = "qlinear µs, TFLOP/s and HBM GB/s at M=1/16/256/1024; % of HBM/MFMA ro
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "int8": 5000.0}
 VARIANTS = (("int8_w8a16", "w8a16", "int8", "per_channel"),
-            ("fp8_w8a8_static", "w8a8_static_fused", "fp8_e4m3fn", "per_tensor"))
+            ("fp8_w8a8_static", "w8a8_static_requant", "fp8_e4m3fn", "per_tensor"))
 NEXT_VARIANTS = (("int8_w8a8_dynamic", "w8a8_dynamic", "int8", "per_channel"),
                  ("int8_linear_routed", "linear_routed", "int8", "per_channel"))
 
@@ -67,6 +69,9 @@ def gemm_bytes(scheme, M, K, N, per_tensor):
       w8a16               N K + scales + 2 M K + 2 M N
       w8a8_static_fused   M <= 16: bf16 x read once by the GEMM: N K + scales + 2 M K + 2 M N
                           M > 16: quantization pass (2 M K read, M K written) + GEMM on codes (M K)
+      w8a8_static_requant GEMM on codes (M K) that also writes the next layer's codes (M N):
+                          N K + scales + M K + 3 M N; a chain adds one quantization pass (3 M K)
+                          for its input and its last call writes no codes (see chain_bytes)
       w8a8_dynamic        quantization pass (2 M K read, M K + 4 M written) + GEMM (M K + 4 M)"""
     scale = 4 if per_tensor else 4 * N
     if scheme == "w8a16":
@@ -75,6 +80,8 @@ def gemm_bytes(scheme, M, K, N, per_tensor):
         return N * K + scale + 2 * M * K + 2 * M * N
     if scheme == "w8a8_static_fused":
         return N * K + scale + 4 * M * K + 2 * M * N
+    if scheme == "w8a8_static_requant":
+        return N * K + scale + M * K + 3 * M * N
     if scheme == "w8a8_dynamic":
         return N * K + scale + 4 * M * K + 8 * M + 2 * M * N
     if scheme == "linear_routed":      # dynamic W8A8 + bias; BF16 fallback (W8A16 bytes) at M <= 32
@@ -82,6 +89,14 @@ def gemm_bytes(scheme, M, K, N, per_tensor):
             return N * K + scale + 2 * M * K + 2 * M * N + 2 * N
         return N * K + scale + 4 * M * K + 8 * M + 2 * M * N + 2 * N
     return N * K + scale + M * K + 2 * M * N
+
+
+def chain_bytes(scheme, M, projs, layers, per_tensor):
+    """Algorithmic bytes of one chain of layers x projs calls."""
+    total = sum(gemm_bytes(scheme, M, K, N, per_tensor) for _, K, N in projs) * layers
+    if scheme == "w8a8_static_requant":
+        total += 3 * M * projs[0][1] - M * projs[-1][2]   # the input's quantization; no codes after the last
+    return total
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_gemm_mfma_int8_w8a16_stack.txt")
@@ -273,6 +288,7 @@ def main():
         x0[M] = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     hbuf = [torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.bfloat16, device=dev) for _ in range(2)]
     xqbuf = torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.uint8, device=dev)
+    cbuf = [torch.empty(Mmax * synth.INTERMEDIATE, dtype=torch.uint8, device=dev) for _ in range(2)]
     sxbuf = torch.empty(Mmax, dtype=torch.float32, device=dev)
     ws_need = 0
     for _, scheme, qtype, _ in VARIANTS + NEXT_VARIANTS:
@@ -280,6 +296,8 @@ def main():
             for _, K, N in synth.STACK_PROJS:
                 if scheme == "linear_routed":
                     ws_need = max(ws_need, qlq.linear_workspace_bytes("w8a8_dynamic", M, K, N, qtype))
+                elif scheme == "w8a8_static_requant":
+                    ws_need = max(ws_need, qlq.workspace_bytes("w8a8_static", M, K, N, qtype))
                 else:
                     ws_need = max(ws_need, qlq.workspace_bytes(scheme, M, K, N, qtype))
     ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
@@ -290,12 +308,26 @@ def main():
         scheme = scheme_of[vname]
         h = x0[M]
         i = 0
+        P = len(synth.STACK_PROJS)
+        if scheme == "w8a8_static_requant":            # the chain's input: one quantization pass
+            K0 = synth.STACK_PROJS[0][1]
+            xq = qlq.quantize_act_static(h, sx[0][0], "fp8_e4m3fn", out=cbuf[1][: M * K0].view(M, K0))
         for l in range(L):
             for p, (_, K, N) in enumerate(synth.STACK_PROJS):
                 out = hbuf[i % 2][: M * N].view(M, N)
                 qw = variants[vname][l][p]
                 if scheme == "w8a16":
                     qlq.qlinear_w8a16(h, qw, out=out, workspace=ws)
+                elif scheme == "w8a8_static_requant":
+                    # this layer's epilogue writes the codes of its output at the next layer's scale
+                    last = l == L - 1 and p == P - 1
+                    if last:
+                        qlq.qlinear_w8a8_static(xq, sx[l][p], qw, out=out, workspace=ws)
+                    else:
+                        nxt = sx[l][p + 1] if p + 1 < P else sx[l + 1][0]
+                        _, xq = qlq.qlinear_w8a8_static_requant(xq, sx[l][p], qw, nxt, out=out,
+                                                                out_codes=cbuf[i % 2][: M * N].view(M, N),
+                                                                workspace=ws)
                 elif scheme == "w8a8_static_fused":
                     qlq.qlinear_w8a8_static_fused(h, sx[l][p], qw, out=out, workspace=ws)
                 elif scheme == "linear_routed":
@@ -363,7 +395,7 @@ def main():
             for M in Ms:
                 us = sum(a.elapsed_time(b) for a, b in ev[(vname, M)]) * 1e3 / args.steps
                 flops = sum(2 * M * N * K for _, K, N in synth.STACK_PROJS) * L
-                byts = sum(gemm_bytes(scheme, M, K, N, gran == "per_tensor") for _, K, N in synth.STACK_PROJS) * L
+                byts = chain_bytes(scheme, M, synth.STACK_PROJS, L, gran == "per_tensor")
                 dt = "bf16" if (scheme == "w8a16" or (scheme == "linear_routed" and M <= 32)) else \
                     ("fp8" if qtype == "fp8_e4m3fn" else "int8")
                 t_hbm = byts / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -417,7 +449,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp8", "data": "synthetic",
             "config": {"workload": f"3B-scale linear stack: {L} layers x {{q_proj 2048->2048, up_proj "
                                    f"2048->11008, down_proj 11008->2048}} chained; INT8 W8A16 and FP8 W8A8 "
-                                   f"static; M in {{1,16,256,1024}}; one HIP graph per chain",
+                                   f"static (each epilogue also writes the next layer's activation codes); "
+                                   f"M in {{1,16,256,1024}}; one HIP graph per chain",
                        "layers": L, "M": list(Ms), "variants": [v[0] for v in VARIANTS],
                        "gemms_per_step": 3 * L * len(cases)},
             "cases": out_cases, "roofline": roof,
