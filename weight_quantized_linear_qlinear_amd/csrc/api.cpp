@@ -74,21 +74,26 @@ namespace {
 
 // Direct-to-LDS MFMA kernel: choose the tile configuration and split-K factor
 // that minimise the estimated time on 256 CUs:
-//   rounds x (K stages per slice x t + e) + split-K (partial bytes x a + S x b),
-// where a round is one wave of resident workgroups.  t (per 64-input tile of K),
-// e (per round: prologue, epilogue, launch) and a, b were fitted to MI355X
+//   rounds x (K stages per slice x t x load + e) + split-K (partial bytes x a + S x b),
+// where a round is one wave of resident workgroups and load = 0.65 + 0.35 x the
+// fraction of CUs the grid keeps busy (a part of the per-stage time is shared
+// bandwidth that a partly filled chip gives to fewer CUs).  t (per 64-input tile
+// of K), e (per round: prologue, epilogue, launch) and a, b were fitted to MI355X
 // timings of every (configuration, split) at the 3B-scale stack's shapes, M = 256
 // and 1024, with cold weights; in total, the fit's picks are within 1 % of the
 // fastest measured plans.
 GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
   constexpr int64_t kCUs = 256;
   const int64_t KT = cdiv(K, 64);
-  constexpr int kCfgs = 6;
-  // {W8A16, W8A8} x cfg 0..5 (cfg 5 is W8A8 only)
-  const double t_us[2][kCfgs] = {{0.913, 0.664, 0.857, 0.677, 1.205, 0.0}, {0.634, 0.464, 0.573, 0.327, 0.905, 0.671}};
-  const double e_us[2][kCfgs] = {{5.495, 2.85, 5.437, 3.227, 12.688, 0.0}, {1.811, 2.127, 1.282, 0.94, 6.234, 7.003}};
-  const double a_us_per_mb[2] = {0.098, 0.142}, b_us[2] = {1.471, 1.669};
-  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1}, {1, 2, 1, 1, 1, 1}};
+  constexpr int kCfgs = 8;
+  // {W8A16, W8A8} x cfg 0..7 (cfgs 5 and 6 are W8A8 only)
+  const double t_us[2][kCfgs] = {{1.128, 0.762, 1.048, 0.769, 1.63, 0.0, 0.0, 1.589},
+                                 {0.788, 0.63, 0.7, 0.377, 1.238, 0.92, 0.772, 1.089}};
+  const double e_us[2][kCfgs] = {{6.856, 3.718, 7.23, 4.537, 15.074, 0.0, 0.0, 12.279},
+                                 {2.692, 2.336, 2.572, 1.696, 7.413, 8.345, 5.552, 7.077}};
+  const double a_us_per_mb[2] = {0.036, 0.096}, b_us[2] = {1.569, 1.813};
+  constexpr double kLoadWeight = 0.35;   // share of t that scales with the fraction of CUs busy
+  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1, 1, 1}, {1, 2, 1, 1, 1, 1, 1, 1}};
   const int sch = scheme == kW8A16 ? 0 : 1;
   GemmPlan best;
   double best_cost = 1e300;
@@ -103,8 +108,11 @@ GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
       if (S > 1 && (tiles > kMaxSplitTiles || KS / S < 2)) break;
       const int64_t ups = cdiv(KS, S);
       if (cdiv(KS, ups) != S) continue;
-      const int64_t rounds = cdiv(tiles * S, kCUs * per_cu[sch][cfg]);
-      double cost = (double)rounds * ((double)(ups * BKT) * t_us[sch][cfg] + e_us[sch][cfg]);
+      const int64_t slots = kCUs * per_cu[sch][cfg];
+      const int64_t rounds = cdiv(tiles * S, slots);
+      const double busy = std::min(1.0, (double)(tiles * S) / (double)slots);
+      const double load = (1.0 - kLoadWeight) + kLoadWeight * busy;
+      double cost = (double)rounds * ((double)(ups * BKT) * t_us[sch][cfg] * load + e_us[sch][cfg]);
       if (S > 1) cost += (double)(S * tiles * BM * BN * 8) * 1e-6 * a_us_per_mb[sch] + b_us[sch] * (double)S;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
