@@ -297,7 +297,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 #pragma unroll
             for (int pc = 0; pc < 2 * TN; ++pc)
               if (m == pc * NM / (2 * TN)) bq[c ^ 1][pc >> 1][pc & 1] = b_quarter(bc, q + 1, pc >> 1, pc & 1);
-            if (m % TN == TN - 1) af[c ^ 1][m / TN] = a_step(cur, q + 1, m / TN);
+            if (m < TM) af[c ^ 1][m] = a_step(cur, q + 1, m);   // early in the step: ready by its end
           } else {
 #pragma unroll
             for (int d = 0; d < DPM; ++d)
