@@ -75,25 +75,26 @@ namespace {
 // Direct-to-LDS MFMA kernel: choose the tile configuration and split-K factor
 // that minimise the estimated time on 256 CUs:
 //   rounds x (K stages per slice x t x load + e) + split-K (partial bytes x a + S x b),
-// where a round is one wave of resident workgroups and load = 0.65 + 0.35 x the
-// fraction of CUs the grid keeps busy (a part of the per-stage time is shared
-// bandwidth that a partly filled chip gives to fewer CUs).  t (per 64-input tile
-// of K), e (per round: prologue, epilogue, launch) and a, b were fitted to MI355X
-// timings of every (configuration, split) at the 3B-scale stack's shapes, M = 256
-// and 1024, with cold weights; in total, the fit's picks are within 1 % of the
-// fastest measured plans.
+// where a round is one wave of resident workgroups and load = (1 - w) + w x the
+// fraction of CUs the grid keeps busy (a share w of the per-stage time is shared
+// bandwidth that a partly filled chip gives to fewer CUs; w = 0.2 for W8A16, 0
+// for W8A8).  t (per 64-input tile of K), e (per round: prologue, epilogue,
+// launch), a, b and w were fitted to MI355X timings of every (configuration,
+// split) at the 3B-scale stack's shapes, M = 256 and 1024, with cold weights; in
+// total, the fit's picks are within 1 % of the fastest measured plans.
 GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
   constexpr int64_t kCUs = 256;
   const int64_t KT = cdiv(K, 64);
   constexpr int kCfgs = 8;
   // {W8A16, W8A8} x cfg 0..7 (cfgs 5 and 6 are W8A8 only)
-  const double t_us[2][kCfgs] = {{1.128, 0.762, 1.048, 0.769, 1.63, 0.0, 0.0, 1.589},
-                                 {0.788, 0.63, 0.7, 0.377, 1.238, 0.92, 0.772, 1.089}};
-  const double e_us[2][kCfgs] = {{6.856, 3.718, 7.23, 4.537, 15.074, 0.0, 0.0, 12.279},
-                                 {2.692, 2.336, 2.572, 1.696, 7.413, 8.345, 5.552, 7.077}};
-  const double a_us_per_mb[2] = {0.036, 0.096}, b_us[2] = {1.569, 1.813};
-  constexpr double kLoadWeight = 0.35;   // share of t that scales with the fraction of CUs busy
-  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1, 1, 1}, {1, 2, 1, 1, 1, 1, 1, 1}};
+  const double t_us[2][kCfgs] = {{1.044, 0.7, 0.951, 0.716, 1.445, 0.0, 0.0, 0.617},
+                                 {0.641, 0.473, 0.575, 0.326, 0.926, 0.687, 0.605, 0.471}};
+  const double e_us[2][kCfgs] = {{6.105, 3.393, 6.54, 4.038, 13.98, 0.0, 0.0, 3.455},
+                                 {1.802, 1.925, 1.546, 1.123, 5.992, 6.794, 4.182, 1.882}};
+  const double a_us_per_mb[2] = {0.067, 0.143}, b_us[2] = {1.433, 1.614};
+  // share of t that scales with the fraction of CUs the grid keeps busy
+  const double load_weight[2] = {0.2, 0.0};
+  const int per_cu[2][kCfgs] = {{1, 1, 1, 1, 1, 1, 1, 1}, {1, 2, 1, 1, 1, 1, 1, 2}};
   const int sch = scheme == kW8A16 ? 0 : 1;
   GemmPlan best;
   double best_cost = 1e300;
@@ -111,7 +112,7 @@ GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
       const int64_t slots = kCUs * per_cu[sch][cfg];
       const int64_t rounds = cdiv(tiles * S, slots);
       const double busy = std::min(1.0, (double)(tiles * S) / (double)slots);
-      const double load = (1.0 - kLoadWeight) + kLoadWeight * busy;
+      const double load = (1.0 - load_weight[sch]) + load_weight[sch] * busy;
       double cost = (double)rounds * ((double)(ups * BKT) * t_us[sch][cfg] * load + e_us[sch][cfg]);
       if (S > 1) cost += (double)(S * tiles * BM * BN * 8) * 1e-6 * a_us_per_mb[sch] + b_us[sch] * (double)S;
       if (cost < best_cost - 1e-9) {

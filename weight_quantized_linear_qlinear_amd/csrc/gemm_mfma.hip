@@ -614,7 +614,7 @@ constexpr MfmaCfg kMfmaCfgs[] = {
     {256, 256, 128, 64, 1, 3, true},     // 4: eight waves, two per SIMD
     {256, 256, 128, 64, 2, 2, false},    // 5: eight waves (bf16 x would need 192 KiB of LDS)
     {256, 192, 64, 96, 2, 2, false},     // 6: eight waves 64x96; 192 columns: 58 column tiles at N = 11008
-    {256, 192, 128, 96, 1, 3, true},     // 7: four waves 128x96
+    {128, 128, 128, 32, 1, 4, true},     // 7: four waves 128x32: each weight column dequantized once
 };
 constexpr int kNumMfmaCfgs = sizeof(kMfmaCfgs) / sizeof(kMfmaCfgs[0]);
 
