@@ -11,13 +11,14 @@
 //  * 32x32 MFMAs: v_mfma_f32_32x32x16_bf16 (W8A16), v_mfma_i32_32x32x32_i8 and
 //    v_mfma_f32_32x32x64_f8f6f4 (W8A8);
 //  * operands move global -> LDS with global_load_lds_dwordx4 (no VGPR staging)
-//    into a ring of NSTAGE stages of 64 inputs each; the loop body is
-//    branch-free and the DMA issues and LDS reads are interleaved between the
-//    MFMAs (sched_group_barrier);
-//  * W8A16 is software-pipelined by 16-input step: the dequantization and LDS
-//    reads of step q+1 sit between the MFMAs of step q in a fixed order, and
-//    a stage's last step already prepares step 0 of the next stage, so the
-//    stage barrier never leaves the matrix cores waiting on VALU or LDS;
+//    into a ring of NSTAGE stages of 64 (or 128) inputs each; the loop body is
+//    branch-free;
+//  * the loop is software-pipelined by MFMA step (16 inputs for bf16, 32 for
+//    int8, 64 for fp8): the LDS reads (and, for W8A16, the dequantization) of
+//    step q+1 sit between the MFMAs of step q in a fixed order (sched_barrier
+//    after each MFMA), and a stage's last step already prepares step 0 of the
+//    next stage and issues the DMAs of the stage NSTAGE ahead, so the stage
+//    barrier never leaves the matrix cores waiting on VALU or LDS;
 //  * the bf16 output tile is staged through LDS so global stores are whole
 //    16-byte chunks of rows;
 //  * x rows that fill whole 128-byte lines per stage (bf16 x; 8-bit x with two
@@ -30,13 +31,15 @@
 //    per-lane addresses;
 //  * W8A16 dequantizes B in registers after the LDS read, four codes at a
 //    time: bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
-//  * large per-wave tiles (128 x 64 or 128 x 128) keep LDS traffic within budget.
+//  * per-wave tiles of 128 rows (or 64 with 8 waves) keep LDS traffic within
+//    budget; W8A16 tiles give each wave its own weight columns where they can,
+//    so a column is dequantized once per workgroup (128x128 as 1 x 4 waves).
 //
 // K-slot convention (A and B agree, so the sum over k is unchanged): inside a
-// 64-input stage, chunk c covers inputs 16c .. 16c+15.  For bf16 step (p, j)
+// 64-input tile, chunk c covers inputs 16c .. 16c+15.  For bf16 step (p, j)
 // lane group kg (= lane / 32) holds inputs 16(2p + kg) + 8j .. +7; for int8 step
-// p it holds chunk 2p + kg; for fp8 (one MFMA per stage) it holds chunks 2kg
-// and 2kg + 1.
+// p it holds chunk 2p + kg; for fp8 (one MFMA per 64-input tile) it holds chunks
+// 2kg and 2kg + 1.
 #include "qlq_device.h"
 #include "qlq_launch.h"
 
