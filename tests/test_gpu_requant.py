@@ -25,10 +25,11 @@ pytestmark = pytest.mark.gpu
 
 QTYPES = ["int8", "fp8_e4m3fn"]
 # small-M kernel (4/8/16 waves, split-K, unaligned N), direct-to-LDS kernel (staged and
-# direct epilogues, split-K), register-staged kernel (ragged K)
+# direct epilogues, split-K), register-staged kernel (K not a multiple of 64, with and without
+# split-K)
 SHAPES = [(1, 1, 1), (1, 2048, 1024), (1, 2048, 2048), (3, 100, 37), (16, 640, 200), (16, 11008, 128),
           (64, 128, 4096), (130, 4096, 96), (255, 1024, 136), (257, 320, 250), (256, 11008, 256),
-          (1024, 2048, 1024)]
+          (1024, 2048, 1024), (130, 1000, 96), (40, 200, 64), (300, 2000, 300)]
 
 
 def _e4m3_step(v: np.ndarray) -> np.ndarray:
