@@ -15,13 +15,17 @@ from tests.gpu_util import bf16_bits, bf16_to_gpu, bits_to_f64, check_close, cod
 pytestmark = pytest.mark.gpu
 
 QTYPES = ["int8", "fp8_e4m3fn"]
-# (M, K, N): decode and prefill sizes, tails in every dimension, split-K cases; the small-M
+# (M, K, N): decode and prefill sizes, tails in every dimension, split-K cases.  The small-M
 # plans include 4, 8 and 16 waves per workgroup (e.g. (4, 4096, 8192): 8 waves, no split;
-# (5, 4096, 1024): 16 waves, two K slices; (2, 2048, 11008): 4 waves)
+# (1, 16384, 1024): 16 waves, two K slices; (2, 2048, 11008): 4 waves), and the aligned path's
+# every count of 1 to 8 K units per wave, for one and two 64-input tiles per unit (the K = 64 * odd
+# case (1, 1728, 2060) leaves the last FP8 W8A8 unit half past the end of K).
 SHAPES = [(1, 1, 1), (1, 64, 16), (2, 5, 3), (8, 8, 8), (1, 2048, 2048), (3, 100, 37), (16, 640, 200),
           (13, 1000, 300), (16, 11008, 128), (17, 640, 200), (31, 512, 129), (33, 256, 64), (64, 128, 4096),
           (255, 1024, 136), (257, 320, 250), (130, 4096, 96), (128, 64, 128), (4, 4096, 8192), (5, 4096, 1024),
-          (2, 2048, 11008), (512, 512, 1024)]
+          (2, 2048, 11008), (512, 512, 1024), (3, 1792, 2060), (7, 1408, 2060), (9, 1280, 2060),
+          (2, 3584, 2060), (11, 2816, 2060), (6, 2560, 2060), (1, 1728, 2060), (1, 16384, 1024),
+          (5, 1152, 2060)]
 
 
 def _prep(seed, M, K, N, qtype, gran="per_channel"):

@@ -149,8 +149,9 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // across workgroups cost more than they gain (the partial-sum handoff is a
     // few memory round trips) except for narrow, deep weights, and each wave
     // should issue all its loads at once (at most kSmallUnitsPerWave units),
-    // with about 2048 waves or more in the grid.  FP8 W8A8 stops at 8 waves
-    // (its 16-wave build would spill registers).
+    // with more waves only while the grid is small (about 512 waves; 256 for
+    // FP8 W8A8, whose units are twice as long).  FP8 W8A8 stops at 8 waves (its
+    // 16-wave build would spill registers).
     p.kind = 0;
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
     const int64_t KU = cdiv(KT, TPU);
@@ -162,7 +163,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     S = cdiv(KU, ups);
     int64_t W = 4;
     while (W < max_waves && cdiv(ups, W) > kSmallUnitsPerWave) W *= 2;
-    while (W < max_waves && NT * S * W <= 2048) W *= 2;
+    while (W < max_waves && NT * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
     p.S = (int)S;
     p.units_per_split = (int)ups;
     p.units_per_wave = (int)cdiv(ups, W);

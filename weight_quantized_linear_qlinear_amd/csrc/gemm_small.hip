@@ -4,8 +4,9 @@
 // "FP8 W8A16 weight-only quantization", Analysis: the FP8->BF16 dequant GEMM trades
 // weight bandwidth for compute; "Nano-vLLM-MOE" mirror, Llama 3.1 8B section:
 // decode leans on weight bandwidth).  So every weight byte is loaded exactly once
-// with 16-byte coalesced loads (a wave reads one contiguous KiB tile), issued in
-// batches before any arithmetic, and the arithmetic runs on the matrix cores:
+// with 16-byte coalesced loads (a wave reads one contiguous KiB tile per unit), a
+// wave issues the loads of all its units before any arithmetic, each unit's
+// arithmetic waits only for that unit's loads, and it runs on the matrix cores:
 //   W8A16: codes -> bf16(fp32(q) * s[n]) in registers -> v_mfma_f32_16x16x32_bf16
 //   W8A8 INT8: v_mfma_i32_16x16x64_i8 on the codes (exact int32)
 //   W8A8 FP8:  v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3) on the codes
@@ -20,6 +21,8 @@
 // agent-coherent partial stores and a device atomic counter (qlq_device.h).
 #include "qlq_device.h"
 #include "qlq_launch.h"
+
+#include <type_traits>
 
 namespace qlq {
 
@@ -97,45 +100,101 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
   f32x4 accf = {0.f, 0.f, 0.f, 0.f};
   i32x4 acci = {0, 0, 0, 0};
 
-  // All loads of the wave's K slice (at most kUnroll units, see plan_gemm) are
-  // issued before the first wait: one memory round trip per wave.
-  for (int u0 = u_begin; u0 < u_end; u0 += kU) {
-    u32x4 wv[kU][TPU];
-    u32x4 xa[kU][TPU];      // A operand bytes: 16 codes, or 8 bf16 (W8A16: values 0..7)
-    u32x4 xb[kU][TPU];      // W8A16: bf16 values 8 .. 15
+  // A unit's arithmetic: dequantize (W8A16) and feed the MFMA.
+  auto unit_mma = [&](const u32x4 (&wv)[TPU], const u32x4 (&xa)[TPU], const u32x4 (&xb)[TPU]) {
+    if constexpr (SCH == kW8A16) {
+      bf16x8 b0 = dequant8<QT>(wv[0].x, wv[0].y, sc, sc_m128);
+      bf16x8 b1 = dequant8<QT>(wv[0].z, wv[0].w, sc, sc_m128);
+      accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[0]), b0, accf);
+      accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[0]), b1, accf);
+    } else if constexpr (QT == kInt8) {
+      acci = mfma_i8_k64(xa[0], wv[0], acci);
+    } else {
+      accf = mfma_fp8_k128(xa[0], xa[TPU - 1], wv[0], wv[TPU - 1], accf);
+    }
+  };
+
+  if constexpr (FAST) {
+    // Aligned K and x: NU units (wave-uniform, 1..kUnroll) issue all their loads
+    // with no branch in between, then run in order, so each unit's arithmetic waits
+    // only for its own loads (the scheduling barriers keep issue order = unit
+    // order).  A branch around a load would make the wait before the first unit a
+    // wait for all of them.  The buffer range check returns zeros for activation
+    // rows >= M and for the K tile past the end (odd tile count with two tiles per
+    // unit); zero codes and zero activations add +0 to an accumulator that starts
+    // at +0, so the sums are unchanged.  Offsets stay below 2^31: M <= 16 and
+    // K <= 2^24 bound both buffers to 2^29 bytes.
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.w) + (int64_t)nt * a.KT * kTileBytes, 0, a.KT * kTileBytes, kBufferWord3);
+    constexpr int kEsz = SCH == kW8A16 ? 2 : 1;
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), 0, a.M * a.K * kEsz, kBufferWord3);
+    const uint32_t xrow = row_ok ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
+    auto run = [&](int u0, auto nu) {
+      constexpr int NU = decltype(nu)::value;
+      u32x4 wv[NU][TPU], xa[NU][TPU], xb[NU][TPU];
 #pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const bool live = u0 + i < u_end;
+      for (int i = 0; i < NU; ++i) {
 #pragma unroll
-      for (int t = 0; t < TPU; ++t) {
-        const int kt = (u0 + i) * TPU + t;
-        const bool ok = live && kt < a.KT;
-        wv[i][t] = ok ? ld16_stream(wbase + (int64_t)kt * kTileBytes) : (u32x4){0u, 0u, 0u, 0u};
-        xa[i][t] = (u32x4){0u, 0u, 0u, 0u};
-        xb[i][t] = (u32x4){0u, 0u, 0u, 0u};
-        if constexpr (SCH == kW8A16) {
-          if (ok && row_ok)
-            load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, kt * kTileK + g * 16,
-                                 a.K, xa[i][t], xb[i][t]);
-        } else {
-          if (ok && row_ok)
-            xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K,
-                                            kt * kTileK + g * 16, a.K);
+        for (int t = 0; t < TPU; ++t) {
+          const int kt = (u0 + i) * TPU + t;
+          const uint32_t xo = xrow + (uint32_t)(kt * kTileK * kEsz);
+          wv[i][t] = __builtin_amdgcn_raw_buffer_load_b128(wrs, kt * kTileBytes + lane * 16, 0, kCachePolicyNt);
+          xa[i][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0);
+          xb[i][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(xo + 16), 0, 0)
+                                   : (u32x4){0u, 0u, 0u, 0u};
         }
+        __builtin_amdgcn_sched_barrier(0);   // issue order = unit order
+      }
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        unit_mma(wv[i], xa[i], xb[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int u0 = u_begin; u0 < u_end; u0 += kU) {
+      switch (u_end - u0 < kU ? u_end - u0 : kU) {
+        case 1: run(u0, std::integral_constant<int, 1>{}); break;
+        case 2: run(u0, std::integral_constant<int, 2>{}); break;
+        case 3: run(u0, std::integral_constant<int, 3>{}); break;
+        case 4: run(u0, std::integral_constant<int, 4>{}); break;
+        case 5: run(u0, std::integral_constant<int, 5>{}); break;
+        case 6: run(u0, std::integral_constant<int, 6>{}); break;
+        case 7: run(u0, std::integral_constant<int, 7>{}); break;
+        default: run(u0, std::integral_constant<int, 8>{}); break;
       }
     }
+  } else {
+    // Generic path: per-element bounds checks.
+    for (int u0 = u_begin; u0 < u_end; u0 += kU) {
+      u32x4 wv[kU][TPU];
+      u32x4 xa[kU][TPU];      // A operand bytes: 16 codes, or 8 bf16 (W8A16: values 0..7)
+      u32x4 xb[kU][TPU];      // W8A16: bf16 values 8 .. 15
 #pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      if (u0 + i >= u_end) break;
-      if constexpr (SCH == kW8A16) {
-        bf16x8 b0 = dequant8<QT>(wv[i][0].x, wv[i][0].y, sc, sc_m128);
-        bf16x8 b1 = dequant8<QT>(wv[i][0].z, wv[i][0].w, sc, sc_m128);
-        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[i][0]), b0, accf);
-        accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[i][0]), b1, accf);
-      } else if constexpr (QT == kInt8) {
-        acci = mfma_i8_k64(xa[i][0], wv[i][0], acci);
-      } else {
-        accf = mfma_fp8_k128(xa[i][0], xa[i][TPU - 1], wv[i][0], wv[i][TPU - 1], accf);
+      for (int i = 0; i < kU; ++i) {
+        const bool live = u0 + i < u_end;
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) {
+          const int kt = (u0 + i) * TPU + t;
+          const bool ok = live && kt < a.KT;
+          wv[i][t] = ok ? ld16_stream(wbase + (int64_t)kt * kTileBytes) : (u32x4){0u, 0u, 0u, 0u};
+          xa[i][t] = (u32x4){0u, 0u, 0u, 0u};
+          xb[i][t] = (u32x4){0u, 0u, 0u, 0u};
+          if constexpr (SCH == kW8A16) {
+            if (ok && row_ok)
+              load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, kt * kTileK + g * 16,
+                                   a.K, xa[i][t], xb[i][t]);
+          } else {
+            if (ok && row_ok)
+              xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K,
+                                              kt * kTileK + g * 16, a.K);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kU; ++i) {
+        if (u0 + i >= u_end) break;
+        unit_mma(wv[i], xa[i], xb[i]);
       }
     }
   }

@@ -202,6 +202,7 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kCachePolicySc1 = 16;       // sc1: coherent at agent scope
+constexpr int kCachePolicyNt = 2;         // nt: streaming (non-temporal)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufferWord3);
