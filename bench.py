@@ -259,8 +259,8 @@ def main():
                          "profiler byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the quantized linear layer runs on a single MI355X here "
-              "(multi-GPU sharding is described in DESIGN.md, not run). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the quantized linear layer runs on a single MI355X, and "
+              "no multi-GPU sharding is run. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

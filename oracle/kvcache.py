@@ -11,7 +11,7 @@ KV arena 7.00 GiB BF16 -> 3.64 GiB mixed).
 Layout (the pages' KV tensors are per token, per KV head, head_dim D): k and v
 are bf16 [T, H, D] with D a multiple of 32.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * K: for every (token t, head h, group g of 32 consecutive channels),
   s = fp16(fp32(absmax) / 127) -- an fp32 division, then round to nearest even
   into IEEE binary16 -- and codes q = clamp(RNE(k / fp32(s)), -127, 127), the

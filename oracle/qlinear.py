@@ -9,7 +9,7 @@ Conventions (the pages never print them; this is the plainest reading of an
 x is [M, K] (tokens x in-features), W is [N, K] (out x in), y = x W^T is [M, N].
 Activations and outputs are bf16, carried here as uint16 bit patterns.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * symmetric quantization, no zero point; scale = absmax / qmax computed in
   fp32 (one correctly rounded division), qmax = 127 for INT8 and 448 for
   e4m3fn; an all-zero row (or tensor) gets scale 1.0;
