@@ -244,9 +244,9 @@ size_t qlq_linear_workspace_bytes(qlq_scheme scheme, int64_t M, int64_t K, int64
 
 /* ---------------------------------------------------------------- KV cache */
 
-/* KV-cache codec: mixed K-int8 / V-FP8 dynamic per-token quantization ("Nano-vLLM-MoE"
- * README, section "KV cache compression": mixed K int8 + V FP8, K group = 32, float16
- * scales).  K and V are bf16 [T, H, D] (tokens, KV heads, head_dim), D a multiple of
+/* KV-cache codec: K as int8 with a scale per group of 32 channels, V as FP8 with a scale
+ * per token and head, both computed at run time ("Nano-vLLM-MoE" README, section "KV cache
+ * compression", its Setup list: float16 scales).  K and V are bf16 [T, H, D] (tokens, KV heads, head_dim), D a multiple of
  * 32 (at most 1024).  Scales are IEEE binary16 bit patterns.
  *   K, per (t, h, group g of channels 32g .. 32g+31):
  *     k_scales[t,h,g] = fp16(absmax / 127)  (fp32 division, round to nearest even,

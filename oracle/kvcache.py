@@ -2,10 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Source: "Nano-vLLM-MoE" README, section "KV cache compression": Setup (mixed K
-int8 + V FP8, K group = 32, scale dtype float16; dynamic per-token quantization,
-the overview line of the README), the "Historical mixed-KV PPL" table (bytes per
-block 0.5195x BF16 at K group 32) and the Memory table (7B, 512 fixed blocks:
+Source: "Nano-vLLM-MoE" README, section "KV cache compression": its Setup list
+(K as int8 in groups of 32 channels with float16 scales, V as FP8; quantized per
+token at run time, as the README's overview also says), the "Historical
+mixed-KV PPL" table (bytes per block 0.5195x BF16 at K group 32) and the Memory
+table (7B, 512 fixed blocks:
 KV arena 7.00 GiB BF16 -> 3.64 GiB mixed).
 
 Layout (the pages' KV tensors are per token, per KV head, head_dim D): k and v

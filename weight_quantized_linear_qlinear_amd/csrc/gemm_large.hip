@@ -1,8 +1,8 @@
 // Large-M (prefill) quantized GEMM family on the gfx950 matrix cores.
 //
 // Prefill is compute bound ("Nano-vLLM-MOE" mirror, Llama 3.1 8B section: prefill
-// leans on compute; "tiny-vLLM" README, "Quantization Results": prefill is the
-// weakest part of the INT8/W8A8 paths), so each workgroup computes a BM x BN
+// leans on compute; "tiny-vLLM" README, "Quantization Results": the quantized paths
+// lose most of their ground at prefill), so each workgroup computes a BM x BN
 // output tile with 16x16 MFMAs fed from LDS:
 //   W8A16:     weight codes are dequantized once per workgroup while they are
 //              staged (bf16(fp32(q) * s[n])), then v_mfma_f32_16x16x32_bf16

@@ -4,8 +4,8 @@
 // gemm_large.hip.
 //
 // Prefill is compute bound ("Nano-vLLM-MOE" mirror, Llama 3.1 8B section: prefill
-// leans on compute; "tiny-vLLM" README, "Quantization Results": prefill is the
-// weakest part of the INT8/W8A8 paths).  Design for gfx950, from measurements on
+// leans on compute; "tiny-vLLM" README, "Quantization Results": the quantized paths
+// lose most of their ground at prefill).  Design for gfx950, from measurements on
 // the part (32x32 MFMA shapes run at twice the rate of the 16x16 ones for bf16
 // and int8; LDS reads ~128 B/clk/CU; L2 -> LDS ~55 B/clk/CU):
 //  * 32x32 MFMAs: v_mfma_f32_32x32x16_bf16 (W8A16), v_mfma_i32_32x32x32_i8 and

@@ -1,6 +1,6 @@
-// KV-cache codec: mixed K-int8 / V-FP8 dynamic per-token quantization
-// ("Nano-vLLM-MoE" README, section "KV cache compression": mixed K int8 + V
-// FP8, K group = 32, float16 scales).
+// KV-cache codec: K as int8 with a scale per group of 32 channels, V as FP8
+// with a scale per token and head, both computed at run time ("Nano-vLLM-MoE"
+// README, section "KV cache compression", its Setup list: float16 scales).
 //
 // K and V are bf16 [T, H, D] (token, KV head, head_dim; D % 32 == 0).
 //   K: per (t, h, group of 32 channels): s = fp16(absmax / 127) (an fp32
