@@ -16,7 +16,7 @@ Sources ("the pages"):
   quantization" (Setup: Triton FP8->BF16 dequant GEMM with a bf16 x bf16 dot
   accumulating in fp32) and "FP8 W8A8 static quantization" (offline-calibrated
   activation scales; scaled-mm and CUTLASS backends with a custom epilogue;
-  Analysis: the W8A8 kernel matches the BF16-dequant reference numerically).
+  Analysis: the W8A8 kernel agrees in value with the BF16-dequant reference).
 * "Nano-vLLM-MOE" README mirror, section "INT8 量化支持" (INT8 quantization
   support): scheme table (int8_w8a16 / int8_w8a8_static) and key-design list
   (W8A16 dequantizes int8 weights to BF16 for a standard matmul; W8A8 static

@@ -337,7 +337,7 @@ def test_w8a8_epilogue_bruteforce(qtype):
 
 @pytest.mark.parametrize("qtype,gran", [("int8", "per_channel"), ("fp8_e4m3fn", "per_tensor")])
 def test_w8a8_matches_bf16_dequant_reference(qtype, gran):
-    # The pages: the W8A8 kernel "matches the BF16-dequant reference numerically".
+    # The pages check the W8A8 kernel against a BF16-dequant reference and find the values agree.
     w, calib, x = synth.small_inputs(44, 64, 1024, 256)
     q, s = oracle.quantize_weight(w, qtype, gran)
     sx = oracle.calibrate_input_scale(calib, qtype)
