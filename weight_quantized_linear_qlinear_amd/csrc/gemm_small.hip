@@ -1,8 +1,8 @@
 // Small-M (decode, M <= 16) quantized GEMM family.
 //
 // Decode is bound by reading the weights once ("Nano-vLLM-MoE" README, section
-// "FP8 W8A16 weight-only quantization", Analysis: the FP8->BF16 dequant GEMM trades
-// weight bandwidth for compute; "Nano-vLLM-MOE" mirror, Llama 3.1 8B section:
+// "FP8 W8A16 weight-only quantization", Analysis: the FP8->BF16 dequant GEMM spends
+// arithmetic to halve the weight bytes; "Nano-vLLM-MOE" mirror, Llama 3.1 8B section:
 // decode leans on weight bandwidth).  So every weight byte is loaded exactly once
 // with 16-byte coalesced loads (a wave reads one contiguous KiB tile per unit), a
 // wave issues the loads of all its units before any arithmetic, each unit's
