@@ -258,7 +258,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     // of stage t + NSTAGE into the slot of stage t, whose last reader passed
     // the barrier.  Each stage's DMAs get NSTAGE - 1 whole stages to land.
     constexpr int Q = 4 * BKT, NM = TM * TN, DPM = (LOADS + NM - 1) / NM;
-    static_assert(TM >= 2, "W8A16 pipeline shape");
+    static_assert(TM >= 2 && NM >= 3, "W8A16 pipeline shape: the last step schedules its work from MFMA 2 on");
     u32x4 bc[2 * BKT][TN];
     u32x4 af[2][TM];
     u32x2 bq[2][TN][2];
@@ -618,6 +618,7 @@ constexpr MfmaCfg kMfmaCfgs[] = {
     {256, 256, 128, 64, 2, 2, false},    // 5: eight waves (bf16 x would need 192 KiB of LDS)
     {256, 192, 64, 96, 2, 2, false},     // 6: eight waves 64x96; 192 columns: 58 column tiles at N = 11008
     {128, 128, 128, 32, 1, 4, true},     // 7: four waves 128x32: each weight column dequantized once
+    {128, 128, 64, 32, 2, 3, false},     // 8: eight waves 64x32: twice the waves issuing operand DMAs
 };
 constexpr int kNumMfmaCfgs = sizeof(kMfmaCfgs) / sizeof(kMfmaCfgs[0]);
 
