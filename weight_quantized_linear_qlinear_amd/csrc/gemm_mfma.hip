@@ -134,19 +134,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 
   // ---- per-lane DMA source pointers (stage 0 of this slice); each stage adds 64 BKT inputs.
   // LINE_A (an x row of a stage spans whole 128-byte lines): the stage holds x
-  // row-major, [row][line][8 chunks of 16 bytes], chunk c of row r stored at
-  // position c ^ (r % 8) within its line.  One DMA instruction then fetches 8
-  // whole lines (one request per line), and the MFMA reads below stay free of
-  // bank conflicts.  Otherwise (8-bit x, one 64-input tile per stage) A fragment
-  // f of a stage is f = (mb * BKT + kt) * kAFrags + q, in MFMA lane order.
+  // row-major, [row][line][8 chunks of 16 bytes].  One DMA instruction then
+  // fetches 8 whole lines (one request per line).  The chunks are permuted so
+  // that 16 consecutive rows reading the same chunk (one ds_read_b128 pass over
+  // the 64 four-byte banks, 256 bytes) touch 16 distinct 16-byte bank groups:
+  // with one line per row, even and odd rows sit in opposite bank halves and
+  // chunk c of row r goes to position c ^ ((r / 2) % 8); with two or more lines
+  // per row, rows 8..15 of each 16 swap lines 0 <-> 1 (and 2 <-> 3, ...) and
+  // chunk c goes to position c ^ (r % 8).  Otherwise (8-bit x, one 64-input tile
+  // per stage) A fragment f of a stage is f = (mb * BKT + kt) * kAFrags + q, in
+  // MFMA lane order.
   const uint8_t* a_src[A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < A_PER_WAVE; ++i) {
     const int f = wave * A_PER_WAVE + i;                     // DMA instruction index in the stage
     if constexpr (LINE_A) {
       const int slot = f * 8 + (lane >> 3);                  // (row, line) slot, row-major
-      const int r = slot / LINES, line = slot % LINES;
-      const int c = (lane & 7) ^ (r & 7);
+      const int r = slot / LINES;
+      const int line = LINES == 1 ? 0 : (slot % LINES) ^ ((r >> 3) & 1);   // logical line held by this slot
+      const int c = (lane & 7) ^ (LINES == 1 ? (r >> 1) & 7 : r & 7);     // chunk held by this position
       int row = m0 + r;
       row = row < a.M ? row : a.M - 1;                       // rows >= M: harmless duplicate
       a_src[i] = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)row * a.K + (int64_t)st_begin * BKT * kTileK) * T::kAElem +
@@ -215,7 +221,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
   // LINE_A read offset of lane's row in row block i of this wave, 16-byte chunk c of the stage row
   auto a_off = [&](int i, int c) {
     const int r = (wm * TM + i) * 32 + l32;
-    return (r * LINES + (c >> 3)) * 128 + (((c & 7) ^ (l32 & 7)) << 4);
+    if constexpr (LINES == 1) return r * 128 + (((c & 7) ^ ((l32 >> 1) & 7)) << 4);
+    else return (r * LINES + ((c >> 3) ^ ((l32 >> 3) & 1))) * 128 + (((c & 7) ^ (l32 & 7)) << 4);
   };
 
   // ---- W8A16 operand helpers for the software-pipelined loop below
