@@ -65,3 +65,40 @@ def test_kv_dequantize_all_codes_and_scales():
     kd_ref, vd_ref = oracle.kv_dequantize(kq, ks, vq, vs)
     assert np.array_equal(bf16_bits(kd), kd_ref)
     assert np.array_equal(bf16_bits(vd), vd_ref)
+
+
+def _rows_below(abits: int) -> np.ndarray:
+    """bf16 rows of 128 whose four 32-channel groups and whole row all have absmax a (the bf16
+    value with bits `abits`), together holding every bf16 x with |x| <= a, both signs."""
+    mags = np.arange(0, abits + 1, dtype=np.uint16)
+    xs = np.concatenate([mags, mags | np.uint16(0x8000)])
+    per_row = 4 * 31
+    n = -(-xs.size // per_row)
+    fill = np.zeros(n * per_row, np.uint16)
+    fill[:xs.size] = xs
+    fill = fill.reshape(n, 4, 31)
+    rows = np.empty((n, 4, 32), np.uint16)
+    rows[:, :, 0] = abits                             # each group's and the row's absmax
+    rows[:, :, 1:] = fill
+    return rows.reshape(n, 128)
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_kv_quantize_every_bf16_below_absmax(part):
+    # The quantizer's division (x / s with the stored fp16 scale) against the oracle's IEEE
+    # division on every bf16 x with |x| <= absmax, for absmax values across the bf16 range:
+    # subnormals, every binade, the largest finite value, and values whose scale saturates
+    # fp16 or rounds to a tie.
+    exps = list(range(0, 255, 4))
+    abits_all = [0x0001, 0x0003, 0x007F] + [(e << 7) | m for e in exps if e > 0 for m in (0x00, 0x2B, 0x7F)] + [0x7F7F]
+    abits = abits_all[part::4]
+    print(f"kv quantize every x below absmax: part {part}, {len(abits)} absmax values", flush=True)
+    rows = np.concatenate([_rows_below(a) for a in abits])
+    kb = rows.reshape(-1, 1, 128)
+    vb = kb[::-1].copy()
+    q = qlq.kv_quantize(bf16_to_gpu(kb), bf16_to_gpu(vb))
+    kq, ks, vq, vs = oracle.kv_quantize(kb, vb)
+    assert np.array_equal(_u16(q.k_scales), ks)
+    assert np.array_equal(_u16(q.v_scales), vs)
+    assert np.array_equal(q.k_codes.cpu().numpy(), kq)
+    assert np.array_equal(q.v_codes.cpu().numpy(), vq)
