@@ -57,6 +57,38 @@ def test_quantize_act_dynamic_bit_exact(qtype, MK):
     assert np.array_equal(codes(xq), q_ref.view(np.uint8))
 
 
+def _rows_below(abits: int, K: int) -> np.ndarray:
+    """bf16 rows of K whose absmax is a (the bf16 value with bits `abits`), together holding every
+    bf16 x with |x| <= a, both signs."""
+    mags = np.arange(0, abits + 1, dtype=np.uint16)
+    xs = np.concatenate([mags, mags | np.uint16(0x8000)])
+    n = -(-xs.size // (K - 1))
+    rows = np.zeros((n, K), np.uint16)
+    rows[:, 0] = abits
+    fill = np.zeros(n * (K - 1), np.uint16)
+    fill[:xs.size] = xs
+    rows[:, 1:] = fill.reshape(n, K - 1)
+    return rows
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("part", range(2))
+def test_quantize_act_dynamic_every_bf16_below_absmax(qtype, part):
+    # The per-token quantizer divides by its row scale with a refined reciprocal above 2^-100 and
+    # by the IEEE division below: every bf16 x with |x| <= absmax, for absmax values across the
+    # bf16 range (subnormals, whose scales take the IEEE branch, every fourth binade, the largest
+    # finite value), against the oracle's IEEE division, codes and scales bit for bit.
+    abits_all = [0x0001, 0x0003, 0x007F, 0x0A00, 0x0C9A] + [(e << 7) | m for e in range(1, 255, 4)
+                                                            for m in (0x00, 0x2B, 0x7F)] + [0x7F7F]
+    abits = abits_all[part::2]
+    print(f"act dynamic every x below absmax {qtype}: part {part}, {len(abits)} absmax values", flush=True)
+    x = np.concatenate([_rows_below(a, 4096) for a in abits])
+    xq, sx = qlq.quantize_act_dynamic(bf16_to_gpu(x), qtype)
+    q_ref, s_ref = oracle.quantize_act_dynamic(x, qtype)
+    assert np.array_equal(sx.cpu().numpy(), s_ref)
+    assert np.array_equal(codes(xq), q_ref.view(np.uint8))
+
+
 @pytest.mark.parametrize("qtype", QTYPES)
 @pytest.mark.parametrize("MKN", SHAPES)
 def test_w8a8_dynamic_parity(qtype, MKN):

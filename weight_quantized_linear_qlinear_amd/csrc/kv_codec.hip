@@ -10,6 +10,7 @@
 //      scale, so decoding with it inverts the step taken.
 //   V: per (t, h): s = fp16(absmax / 448), codes = e4m3fn_sat(v / fp32(s)).
 //   Decoding: bf16(fp32(q) * fp32(s)), the W8A16 dequantization rule.
+//   The divisions go through RcpDiv (qlq_device.h): same codes, fewer instructions.
 // Stored per (t, h) with D = 128: 128 + 8 bytes of K, 128 + 2 of V, 0.5195 of
 // bf16 -- the bytes-per-block figure of the pages.
 //
@@ -44,26 +45,6 @@ __device__ __forceinline__ uint32_t kv_scale_bits(float absmax, float qmax) {
   return s == 0u ? 1u : s;                                    // 2^-24 instead of a zero scale
 }
 
-// x / s for the codec's operands with the IEEE quotient's codes at about half its
-// cost: a reciprocal refined by one Newton step, then one correction of the product
-// (sign kept for zeros).  Checked exhaustively on gfx950 against the IEEE division:
-// for every positive finite bf16 absmax a, both scales the codec stores for it and
-// every bf16 x with |x| <= a, the int8 and e4m3 codes are identical.  A non-finite x
-// keeps the plain product (inf or NaN, as the division gives).
-struct KvDiv {
-  float s, r;
-  __device__ __forceinline__ explicit KvDiv(float s_) : s(s_) {
-    const float r0 = __builtin_amdgcn_rcpf(s_);
-    r = __builtin_fmaf(__builtin_fmaf(-s_, r0, 1.0f), r0, r0);
-  }
-  __device__ __forceinline__ float operator()(float x) const {
-    const float q0 = x * r;
-    const float rem = __builtin_fmaf(-s, q0, x);
-    const float q1 = __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
-    return rem == rem ? q1 : q0;
-  }
-};
-
 __device__ __forceinline__ float half_max(float v) {          // max over the 32 lanes of a half-wave
   for (int off = 16; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
@@ -94,7 +75,7 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
     if (64 * j + (lane & 32) < D) {                           // the group exists (D % 32 == 0)
       const uint32_t sb = kv_scale_bits(am, 127.0f);
       if ((lane & 31) == 0) ks[(int64_t)row * G + 2 * j + (lane >> 5)] = (uint16_t)sb;
-      kq[base + e] = (uint8_t)f32_to_i8_sat(KvDiv(f16_bits_to_f32(sb))(kf[j]));
+      kq[base + e] = (uint8_t)f32_to_i8_sat(RcpDiv(f16_bits_to_f32(sb))(kf[j]));
     }
   }
   // V: one scale for the whole row
@@ -104,7 +85,7 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
   for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
   const uint32_t sb = kv_scale_bits(am, 448.0f);
   if (lane == 0) vs[row] = (uint16_t)sb;
-  const KvDiv dv(f16_bits_to_f32(sb));
+  const RcpDiv dv(f16_bits_to_f32(sb));
 #pragma unroll
   for (int j = 0; j < JN; ++j) {
     const int e = lane + 64 * j;
@@ -141,7 +122,7 @@ __global__ __launch_bounds__(256) void kv_quantize8_kernel(const uint16_t* __res
     for (int off = 1; off < TPR; off <<= 1) va = fmaxf(va, __shfl_xor(va, off, 64));   // V row: TPR lanes
     if (!live) continue;
     const uint32_t kb = kv_scale_bits(ka, 127.0f), vb = kv_scale_bits(va, 448.0f);
-    const KvDiv dk(f16_bits_to_f32(kb)), dv(f16_bits_to_f32(vb));
+    const RcpDiv dk(f16_bits_to_f32(kb)), dv(f16_bits_to_f32(vb));
     uint32_t kw[2], vw[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -188,16 +188,25 @@ __global__ __launch_bounds__(256) void quant_act_dynamic_kernel(const uint16_t* 
   if (!live) return;
   const float s = scale_of(am, QT == kFp8 ? 448.0f : 127.0f);
   if (t == 0) x_scale[m] = s;
+  // every x of the row is within its absmax, so RcpDiv gives the IEEE codes for
+  // s >= 2^-100 (row-uniform branch; tinier rows keep the division)
+  auto emit = [&](auto q4) {
 #pragma unroll
-  for (int j = 0; j < kCache; ++j) {
-    const int i = t + j * T;
-    if (i < nvec)
-      *reinterpret_cast<u32x2*>(out + i * 8) =
-          (u32x2){quant4<QT>(cache[j].x, cache[j].y, s), quant4<QT>(cache[j].z, cache[j].w, s)};
-  }
-  for (int i = t + kCache * T; i < nvec; i += T) {
-    const u32x4 v = ld16(row + i * 8);
-    *reinterpret_cast<u32x2*>(out + i * 8) = (u32x2){quant4<QT>(v.x, v.y, s), quant4<QT>(v.z, v.w, s)};
+    for (int j = 0; j < kCache; ++j) {
+      const int i = t + j * T;
+      if (i < nvec)
+        *reinterpret_cast<u32x2*>(out + i * 8) = (u32x2){q4(cache[j].x, cache[j].y), q4(cache[j].z, cache[j].w)};
+    }
+    for (int i = t + kCache * T; i < nvec; i += T) {
+      const u32x4 v = ld16(row + i * 8);
+      *reinterpret_cast<u32x2*>(out + i * 8) = (u32x2){q4(v.x, v.y), q4(v.z, v.w)};
+    }
+  };
+  if (s >= 0x1p-100f) {
+    const RcpDiv dv(s);
+    emit([&](uint32_t lo, uint32_t hi) { return quant4_rcp<QT>(lo, hi, dv); });
+  } else {
+    emit([&](uint32_t lo, uint32_t hi) { return quant4<QT>(lo, hi, s); });
   }
   for (int k = nvec * 8 + t; k < K; k += T) {
     const float v = bf16_bits_to_f32(row[k]) / s;
