@@ -67,12 +67,16 @@ def test_calibrate_input_scale_bit_exact(qtype):
 
 @pytest.mark.parametrize("qtype", QTYPES)
 def test_quantize_act_exhaustive_bf16_patterns(qtype):
-    # every finite bf16 value, at scale 1 and at an awkward scale
+    # every finite bf16 value, at an awkward scale (the IEEE division) and at calibrated scales
+    # fp32(a / qmax) for bf16 a (1 = 127 / 127 among them), which take the refined-reciprocal
+    # division: tiny, huge and ordinary a, both qmax, so most x lie far beyond the absmax
     allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     vals = oracle.bf16_bits_to_f32(allb)
     fin = allb[np.isfinite(vals)]
     x = np.concatenate([fin, np.zeros((-fin.size) % 256, np.uint16)]).reshape(-1, 256)
-    for s in [1.0, float(np.float32(0.0123456))]:
+    calibrated = [oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(np.array([a], np.float32)))[0] / np.float32(q)
+                  for a, q in [(3.0, 127), (0.07, 448), (1e-28, 127), (3e38, 448), (0.5, 448), (448.0, 127)]]
+    for s in [1.0, float(np.float32(0.0123456))] + [float(np.float32(c)) for c in calibrated]:
         got = codes(qlq.quantize_act_static(bf16_to_gpu(x), s, qtype))
         ref = oracle.quantize_act_static(x, np.float32(s), qtype).view(np.uint8)
         assert np.array_equal(got, ref), f"scale {s}: {np.count_nonzero(got != ref)} codes differ"

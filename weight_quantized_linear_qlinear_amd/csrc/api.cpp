@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "qlq_launch.h"
@@ -45,6 +46,27 @@ constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
 constexpr int64_t kSmallUnitsPerWave = 8;   // matches kUnroll of the small-M kernel
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// True when s = fp32(a / qmax) for a positive finite bf16 a and qmax 127 or 448 (how
+// calibration and the per-token quantizer form scales) and s >= 2^-100: the scales for
+// which the kernels' refined-reciprocal division (RcpDivAny) was checked to give the
+// IEEE division's codes for every bf16 x.  Other scales keep the IEEE division.
+bool calibrated_scale(float s) {
+  if (!std::isfinite(s) || !(s >= 0x1p-100f)) return false;
+  for (const float qmax : {127.0f, 448.0f}) {
+    const float guess = s * qmax;
+    uint32_t bits;
+    std::memcpy(&bits, &guess, sizeof bits);
+    const int64_t hi = bits >> 16;
+    for (int d = -2; d <= 2; ++d) {
+      const uint32_t cb = (uint32_t)(hi + d) << 16;
+      float c;
+      std::memcpy(&c, &cb, sizeof c);
+      if (std::isfinite(c) && c > 0.0f && c / qmax == s) return true;
+    }
+  }
+  return false;
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -295,7 +317,8 @@ qlq_status qlq_quantize_act_static(const void* x_bf16, int64_t M, int64_t K, flo
   if (qlq_status st = check_qtype(qtype)) return st;
   if (qlq_status st = check_scale(input_scale, "input_scale")) return st;
   if (!aligned(x_bf16, 2)) return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
-  return hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream),
+  return hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream,
+                                          calibrated_scale(input_scale)),
                     "quantize_act_static");
 }
 
@@ -356,6 +379,7 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.bias = static_cast<const uint16_t*>(bias);
   a.y_codes = static_cast<uint8_t*>(y_codes);
   a.next_scale = next_scale;
+  a.next_scale_rcp = (y_codes && calibrated_scale(next_scale)) ? 1 : 0;
   a.out_acc = out_acc;
   a.fast = fast;
   hipError_t e = plan.kind == 0   ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
@@ -425,7 +449,8 @@ qlq_status qlq_qlinear_w8a8_static_fused(const void* x_bf16, float input_scale, 
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   void* xq = static_cast<uint8_t*>(workspace) + off;
-  if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream),
+  if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream,
+                                          calibrated_scale(input_scale)),
                                  "qlinear_w8a8_static_fused"))
     return st;
   return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale, nullptr,
@@ -517,7 +542,8 @@ qlq_status qlq_linear(qlq_scheme scheme, const void* x_bf16, int64_t M, int64_t 
   void* xq = static_cast<uint8_t*>(workspace) + off;
   const float* rows = nullptr;
   if (scheme == QLQ_SCHEME_W8A8_STATIC) {
-    if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream), "linear"))
+    if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream,
+                                          calibrated_scale(input_scale)), "linear"))
       return st;
   } else {
     float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(xq) + ((size_t)M * (size_t)K + 255) / 256 * 256);

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a, int S, i
         } else {
           const float v = T::kIntAcc ? (float)acci[i][j][jj] : accf[i][j][jj];
           const float comb = (a.row_scale ? a.row_scale[m] : a.input_scale) * sw;   // fp32(s_x * s_w[n])
-          store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale);
+          store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale, a.next_scale_rcp);
         }
       }
   }

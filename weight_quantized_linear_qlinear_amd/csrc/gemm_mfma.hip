@@ -539,6 +539,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     }
     __syncthreads();
     constexpr int CH = BN / 8;                               // 16-byte chunks per row
+    const RcpDivAny dvn(a.next_scale_rcp ? a.next_scale : 1.0f);
 #pragma unroll 4
     for (int c = tid; c < BM * CH; c += NT) {
       const int row = c / CH, ch = c % CH;
@@ -554,7 +555,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
           for (int e = 0; e < a.N - n; ++e) dst[e] = src[e];
         }
         if (SCH == kW8A8 && a.y_codes) {                     // next layer's codes of these 8 outputs
-          const u32x2 q = {quant4<QT>(v.x, v.y, a.next_scale), quant4<QT>(v.z, v.w, a.next_scale)};
+          const u32x2 q = a.next_scale_rcp ? (u32x2){quant4_rcp<QT>(v.x, v.y, dvn), quant4_rcp<QT>(v.z, v.w, dvn)}
+                                           : (u32x2){quant4<QT>(v.x, v.y, a.next_scale), quant4<QT>(v.z, v.w, a.next_scale)};
           uint8_t* cdst = a.y_codes + (int64_t)m * a.N + n;
           if (n + 8 <= a.N) {
             *reinterpret_cast<u32x2*>(cdst) = q;
@@ -586,7 +588,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
             const float sx = a.row_scale ? a.row_scale[m] : a.input_scale;
             const float comb = sx * (a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n]);
             const float v = T::kIntAcc ? (float)acci[i][j][e] : accf[i][j][e];
-            store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale);
+            store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale, a.next_scale_rcp);
           }
         }
     }

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
     } else {
       const float v = T::kIntAcc ? (float)__builtin_bit_cast(i32x4, tot)[j] : tot[j];
       const float comb = (a.row_scale ? a.row_scale[m] : a.input_scale) * sw;   // fp32(s_x * s_w[n])
-      store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale);
+      store_bf16_requant<QT>(a.y, a.y_codes, o, add_bias(v * comb, a.bias, n), a.next_scale, a.next_scale_rcp);
     }
   }
 }

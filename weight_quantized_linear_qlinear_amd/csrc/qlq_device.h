@@ -94,16 +94,19 @@ __device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s) {
 
 // x / s through a reciprocal refined by one Newton step and one correction of the
 // product (sign kept for zeros; a non-finite x keeps the plain product, inf or NaN
-// as the division gives): about half the IEEE division's instructions.  Only for
-// the quantizers whose x never exceeds the absmax a that s was derived from,
-// where exhaustive runs on gfx950 found the int8 and e4m3 codes identical to the
-// IEEE quotient's for every positive finite bf16 a and every bf16 x with
-// |x| <= a: s = fp16(a / qmax) as the KV codec stores it (qmax 127 and 448), and
-// s = fp32(a / qmax) >= 2^-100 as the per-token quantizer computes it.  Larger
-// |x| (a caller's static scale) or smaller s fall outside what was checked.
-struct RcpDiv {
+// as the division gives): about half the IEEE division's instructions.  Exhaustive
+// runs on gfx950 found the int8 and e4m3 codes identical to the IEEE quotient's
+// for every positive finite bf16 a and every bf16 x with |x| <= a, for the scales
+// s = fp16(a / qmax) the KV codec stores (qmax 127 and 448) and s = fp32(a / qmax)
+// >= 2^-100 (how the per-token quantizer and calibration form scales).  With
+// ANY_X, quotients of magnitude >= 1024 (they saturate either code) keep the plain
+// product, and the codes matched for every finite bf16 x whatever its magnitude,
+// for the second kind of scale: the static quantizer and the requantizing epilogue
+// use it when the host finds the caller's scale to be of that kind.
+template <bool ANY_X>
+struct RcpDivT {
   float s, r;
-  __device__ __forceinline__ explicit RcpDiv(float s_) : s(s_) {
+  __device__ __forceinline__ explicit RcpDivT(float s_) : s(s_) {
     const float r0 = __builtin_amdgcn_rcpf(s_);
     r = __builtin_fmaf(__builtin_fmaf(-s_, r0, 1.0f), r0, r0);
   }
@@ -111,13 +114,16 @@ struct RcpDiv {
     const float q0 = x * r;
     const float rem = __builtin_fmaf(-s, q0, x);
     const float q1 = __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
+    if constexpr (ANY_X) return (rem == rem && __builtin_fabsf(q0) < 1024.0f) ? q1 : q0;
     return rem == rem ? q1 : q0;
   }
 };
+using RcpDiv = RcpDivT<false>;
+using RcpDivAny = RcpDivT<true>;
 
 // quant4 with the division above (same codes within its checked domain).
-template <int QT>
-__device__ __forceinline__ uint32_t quant4_rcp(uint32_t lo, uint32_t hi, const RcpDiv& dv) {
+template <int QT, class DIV>
+__device__ __forceinline__ uint32_t quant4_rcp(uint32_t lo, uint32_t hi, const DIV& dv) {
   float a = dv(bf16_bits_to_f32(lo & 0xFFFF)), b = dv(bf16_bits_to_f32(lo >> 16));
   float c = dv(bf16_bits_to_f32(hi & 0xFFFF)), d = dv(bf16_bits_to_f32(hi >> 16));
   if constexpr (QT == kFp8) return f32x4_to_e4m3x4_sat(a, b, c, d);
@@ -133,12 +139,22 @@ __device__ __forceinline__ uint32_t quant1(uint32_t b, float s) {
 }
 
 // bf16 output element y[o] = bf16(val) and, with a code buffer, codes[o] = the
-// activation code of that bf16 value at scale s (requantization for the next layer).
+// activation code of that bf16 value at scale s (requantization for the next layer),
+// through RcpDivAny when `rcp` is set (s of the checked kind).
 template <int QT>
-__device__ __forceinline__ void store_bf16_requant(void* y, uint8_t* codes, int64_t o, float val, float s) {
+__device__ __forceinline__ void store_bf16_requant(void* y, uint8_t* codes, int64_t o, float val, float s,
+                                                   bool rcp = false) {
   const __bf16 h = (__bf16)val;
   reinterpret_cast<__bf16*>(y)[o] = h;
-  if (codes) codes[o] = (uint8_t)quant1<QT>(__builtin_bit_cast(uint16_t, h), s);
+  if (codes) {
+    const uint32_t b = __builtin_bit_cast(uint16_t, h);
+    if (rcp) {
+      const float v = RcpDivAny(s)(bf16_bits_to_f32(b));
+      codes[o] = (uint8_t)(QT == kFp8 ? (f32x4_to_e4m3x4_sat(v, 0.0f, 0.0f, 0.0f) & 0xFFu) : f32_to_i8_sat(v));
+    } else {
+      codes[o] = (uint8_t)quant1<QT>(b, s);
+    }
+  }
 }
 
 // Dequantize 8 codes (two dwords) to 8 bf16 = bf16(fp32(q) * s), one fp32

@@ -45,6 +45,7 @@ struct GemmArgs {
   const uint16_t* bias;     // bf16 bias [N] added before the bf16 rounding, or null
   uint8_t* y_codes;         // W8A8: codes [M,N] of the bf16 output at next_scale (the next
   float next_scale;         //   layer's static activation quantization), or null
+  int next_scale_rcp = 0;   // next_scale is fp32(a / qmax) for a bf16 a: RcpDivAny is exact
   int out_acc;
   int fast;                 // K % 64 == 0 and 16-byte aligned rows/pointers
 };
@@ -66,7 +67,8 @@ hipError_t launch_absmax_scale(const void* src, int is_bf16, int64_t numel, floa
 hipError_t launch_pack_weight(const void* w, int is_bf16, int N, int K, int qtype, int per_tensor,
                               uint8_t* packed, float* w_scale, hipStream_t st);
 hipError_t launch_unpack_weight(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st);
-hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st);
+hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st,
+                            bool rcp = false);
 hipError_t launch_kv_quantize(const void* k, const void* v, int64_t rows, int D, void* kq, void* ks, void* vq,
                               void* vs, hipStream_t st);
 hipError_t launch_kv_dequantize(const void* kq, const void* ks, const void* vq, const void* vs, int64_t numel, int D,

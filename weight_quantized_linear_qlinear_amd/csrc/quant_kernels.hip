@@ -123,14 +123,23 @@ __global__ __launch_bounds__(256) void unpack_weight_kernel(const uint8_t* packe
 // store); element by element for the tail or unaligned buffers.
 template <int QT>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* x, int64_t numel, float s,
-                                                        uint8_t* xq, int vec_ok) {
+                                                        uint8_t* xq, int vec_ok, int rcp) {
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t nvec = vec_ok ? numel / 8 : 0;
-  for (int64_t i = tid; i < nvec; i += stride) {
-    u32x4 v = ld16(x + i * 8);
-    u32x2 o = {quant4<QT>(v.x, v.y, s), quant4<QT>(v.z, v.w, s)};
-    *reinterpret_cast<u32x2*>(xq + i * 8) = o;
+  if (rcp) {                                                 // s of the kind RcpDivAny was checked for
+    const RcpDivAny dv(s);
+    for (int64_t i = tid; i < nvec; i += stride) {
+      u32x4 v = ld16(x + i * 8);
+      u32x2 o = {quant4_rcp<QT>(v.x, v.y, dv), quant4_rcp<QT>(v.z, v.w, dv)};
+      *reinterpret_cast<u32x2*>(xq + i * 8) = o;
+    }
+  } else {
+    for (int64_t i = tid; i < nvec; i += stride) {
+      u32x4 v = ld16(x + i * 8);
+      u32x2 o = {quant4<QT>(v.x, v.y, s), quant4<QT>(v.z, v.w, s)};
+      *reinterpret_cast<u32x2*>(xq + i * 8) = o;
+    }
   }
   for (int64_t i = nvec * 8 + tid; i < numel; i += stride) {
     float v = bf16_bits_to_f32(x[i]) / s;
@@ -253,15 +262,15 @@ hipError_t launch_unpack_weight(const uint8_t* packed, int N, int K, uint8_t* ou
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st) {
+hipError_t launch_quant_act(const void* x, int64_t numel, float s, int qtype, void* xq, hipStream_t st, bool rcp) {
   int vec_ok = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && ((reinterpret_cast<uintptr_t>(xq) & 7) == 0);
   int grid = grid_for(vec_ok ? numel / 8 + 1 : numel, 256, 8192);
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
   uint8_t* out = reinterpret_cast<uint8_t*>(xq);
   if (qtype == kFp8)
-    quant_act_kernel<kFp8><<<grid, 256, 0, st>>>(xs, numel, s, out, vec_ok);
+    quant_act_kernel<kFp8><<<grid, 256, 0, st>>>(xs, numel, s, out, vec_ok, rcp ? 1 : 0);
   else
-    quant_act_kernel<kInt8><<<grid, 256, 0, st>>>(xs, numel, s, out, vec_ok);
+    quant_act_kernel<kInt8><<<grid, 256, 0, st>>>(xs, numel, s, out, vec_ok, rcp ? 1 : 0);
   return hipGetLastError();
 }
 
