@@ -156,6 +156,107 @@ def build_stack(qlq, synth, torch, dev, seed, layers):
     return qi, qf, [[sx[3 * l + p] for p in range(3)] for l in range(layers)]
 
 
+COLD_BYTES = 1 << 30       # rotated buffer sets per single-GEMM workload: past the 256 MB MALL and the L2s
+
+
+def single_gemm_rows(qlq, synth, torch, dev, min_launches=200, warmup=3):
+    """The four single-GEMM workloads (the pages' microbench shapes), each as one call
+    of the library per launch.
+
+    Cold (primary): R independent {packed W, scales, x, y} sets totalling >= 1 GiB, one
+    launch per set in a captured graph, so every launch reads its weights from HBM.
+    Hot (secondary): the same graph over one set (weights resident in the MALL/L2;
+    comparable to the pages' cache-resident microbench, not an HBM figure).  Each graph
+    is replayed until >= min_launches launches were timed; figures are per launch,
+    with p10/p50/p90 over the replays.  W8A8 rows time the GEMM on codes
+    (qlinear_w8a8_static) and, as `layer`, the one-call static W8A8 layer from bf16 x
+    (quantization pass + GEMM, qlinear_w8a8_static_fused)."""
+    import numpy as np
+    res = {}
+    stream = torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    for idx, (name, c) in enumerate(synth.CASES.items()):
+        inp = synth.case_inputs(c)
+        qw = qlq.quantize_weight(torch.from_numpy(inp.w).to(dev), c.qtype, c.granularity)
+        x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).view(torch.bfloat16).to(dev)
+        w8a8 = c.scheme != "w8a16"
+        M, K, N = c.M, c.K, c.N
+        sx = 1.0
+        if w8a8:
+            cal = torch.from_numpy(np.ascontiguousarray(inp.calib).view(np.int16)).view(torch.bfloat16).to(dev)
+            sx = qlq.calibrate_input_scale(cal, c.qtype).item()
+        per_tensor = c.granularity == "per_tensor"
+        set_bytes = qw.packed.numel() + 4 * qw.scale.numel() + 2 * M * K + 2 * M * N
+        R = max(1, -(-COLD_BYTES // set_bytes))
+        sets = []
+        for _ in range(R):
+            w_r = qlq.QuantizedWeight(qw.packed.clone(), qw.scale.clone(), qw.N, qw.K, qw.qtype, qw.granularity)
+            x_r = x.clone()
+            xq_r = qlq.quantize_act_static(x_r, sx, c.qtype) if w8a8 else None
+            sets.append((w_r, x_r, xq_r, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        ws_need = qlq.workspace_bytes("w8a8_static_fused" if w8a8 else "w8a16", M, K, N, c.qtype)
+        ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
+
+        def call(kind, st):
+            w_r, x_r, xq_r, y_r = st
+            if kind == "gemm" and not w8a8:
+                qlq.qlinear_w8a16(x_r, w_r, out=y_r, workspace=ws)
+            elif kind == "gemm":
+                qlq.qlinear_w8a8_static(xq_r, sx, w_r, out=y_r, workspace=ws)
+            else:
+                qlq.qlinear_w8a8_static_fused(x_r, sx, w_r, out=y_r, workspace=ws)
+
+        row = {"config": idx, "scheme": c.scheme, "qtype": c.qtype, "M": M, "K": K, "N": N, "cold_sets": R,
+               "cold_bytes": R * set_bytes}
+        flops = 2 * M * N * K
+        for kind in (("gemm", "layer") if w8a8 else ("gemm",)):
+            byts = N * K + (4 if per_tensor else 4 * N) + 2 * M * N + (2 * M * K if not w8a8 else M * K)
+            if kind == "layer":
+                byts += 3 * M * K
+            dt = "bf16" if not w8a8 else ("fp8" if c.qtype == "fp8_e4m3fn" else "int8")
+            for temp, picks in (("cold", sets), ("hot", [sets[0]] * R)):
+                for st in picks[:2]:
+                    call(kind, st)                      # eager warm-up (and LDS limits) outside capture
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for st in picks:
+                        call(kind, st)
+                reps = max(3, -(-min_launches // R))
+                for _ in range(warmup):
+                    g.replay()
+                evs = []
+                for _ in range(reps):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(cur)
+                    g.replay()
+                    e1.record(cur)
+                    evs.append((e0, e1))
+                torch.cuda.synchronize()
+                per = np.array([a.elapsed_time(b) * 1e3 / R for a, b in evs])
+                us = float(per.mean())
+                t_hbm = byts / (HBM_PEAK_GBS * 1e9) * 1e6
+                t_mfma = flops / (MFMA_PEAK_TFLOPS[dt] * 1e12) * 1e6
+                key = f"{kind}_{temp}"
+                row[key] = {"us": round(us, 3), "p10_us": round(float(np.percentile(per, 10)), 3),
+                            "p50_us": round(float(np.percentile(per, 50)), 3),
+                            "p90_us": round(float(np.percentile(per, 90)), 3),
+                            "launches": int(R * reps), "tflops": round(flops / us / 1e6, 3),
+                            "gbs": round(byts / us / 1e3, 1), "algorithmic_bytes": int(byts),
+                            "hbm_frac": round(t_hbm / us, 3), "mfma_frac": round(t_mfma / us, 3),
+                            "bound": "hbm" if t_hbm >= t_mfma else "mfma"}
+                if temp == "hot":
+                    row[key]["note"] = "one buffer set: MALL/L2-resident, not an HBM figure"
+                del g
+        res[f"config{idx}/{name}"] = row
+        del sets, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log(f"[bench] single GEMM {name}: cold {row['gemm_cold']['us']} us over {R} sets")
+    return res
+
+
 KV_LAYERS, KV_HEADS, KV_DIM = 28, 4, 128
 KV_TOKENS = (1, 16, 256, 1024, 8192, 32768)     # new tokens per step up to a 32K context read
 
@@ -420,6 +521,8 @@ def main():
     out_cases, tot_flops = figures(VARIANTS, groups)
     next_cases_out, _ = figures(NEXT_VARIANTS)
     next_cases_out.update(kv_rows(qlq, torch, dev, KV_TOKENS, args.steps, args.warmup))
+    single = single_gemm_rows(qlq, synth, torch, dev)
+    out_cases.update(single)
     # dominant kernel: the (variant, kernel family) group with the most time
     fam, g = max(groups.items(), key=lambda kv: kv[1]["us"])
     avg_us = g["us"] / g["launches"]

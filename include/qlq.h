@@ -268,6 +268,31 @@ qlq_status qlq_kv_dequantize(const void* k_codes, const void* k_scales, const vo
                              const void* v_scales, int64_t T, int64_t H, int64_t D,
                              void* k_bf16, void* v_bf16, hipStream_t stream);
 
+/* ------------------------------------------------------------- test hooks */
+
+/* The launch plan a GEMM call takes for these sizes when x is 16-byte aligned (what
+ * the tests use to show which kernel configuration a case reaches).  kind 0 is the
+ * small-M family (M <= 16; tile_m = tile_n = 16, `waves` waves per workgroup), 1 the
+ * register-staged large-M kernel (K not a multiple of 64), 2 the direct-to-LDS
+ * large-M kernel with tile configuration `cfg` (-1 otherwise).  split_k is the
+ * number of K slices per output tile, grid the workgroups launched and
+ * workspace_bytes what the call needs (0 without split-K).  Host only: nothing is
+ * enqueued.  Errors as for the GEMM calls' size and enum checks. */
+typedef struct {
+  int32_t kind, cfg, split_k, tile_m, tile_n, waves, grid;
+  int64_t workspace_bytes;
+} qlq_plan_info;
+qlq_status qlq_gemm_plan(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype,
+                         qlq_plan_info* info);
+
+/* 1 when the activation quantizers divide by scale s with a reciprocal refined by
+ * one Newton step and one correction of the product instead of the IEEE division:
+ * s = fp32(a / qmax) for a positive finite bf16 a and qmax 127 or 448 (what
+ * calibration and the per-token quantizer produce) and s >= 2^-100.  For those
+ * scales the refined division gives the IEEE quotient's codes for every finite
+ * bf16 x; every other scale keeps the IEEE division (returns 0).  Host only. */
+int qlq_scale_is_calibrated(float s);
+
 /* ------------------------------------------------------------------- errors */
 
 const char* qlq_status_string(qlq_status status);

@@ -225,3 +225,107 @@ def test_validation_of_the_requant_call():
     assert st == 1 and "133144" in msg
     st, _ = _status(f, FAKE, 1.0, 4, 64, 16, FAKE, FAKE, 16, 5, 1.0, FAKE, FAKE, None, 0, None)
     assert st == 2
+
+
+def test_multi_kernel_calls_validate_everything_before_the_first_launch():
+    """The fused static call and the routed Linear enqueue a quantization kernel and
+    then the GEMM.  Every check of the GEMM runs before the first launch: on this
+    host (no GPU) a launch would fail with QLQ_ERR_HIP, so QLQ_ERR_INVALID_ARG with
+    the GEMM's own message shows that nothing was enqueued."""
+    L = qlq.lib()
+    M, K, N = 4, 64, 16
+    mis = ctypes.c_void_p(0x10001)
+    for qtype in (0, 1):
+        need = qlq.workspace_bytes("w8a8_static_fused", M, K, N, "int8" if qtype == 0 else "fp8_e4m3fn")
+        fused = L.qlq_qlinear_w8a8_static_fused
+        st, msg = _status(fused, FAKE, 1.0, M, K, N, FAKE, FAKE, 3, qtype, 0, FAKE, FAKE, need, None)
+        assert st == 1 and "w_scale_numel" in msg, msg
+        st, msg = _status(fused, FAKE, 1.0, M, K, N, FAKE, FAKE, N, qtype, 0, mis, FAKE, need, None)
+        assert st == 1 and "aligned" in msg, msg
+        st, msg = _status(fused, FAKE, 1.0, M, K, N, ctypes.c_void_p(0x10008), FAKE, N, qtype, 0, FAKE, FAKE, need,
+                          None)
+        assert st == 1 and "aligned" in msg, msg
+        st, msg = _status(fused, FAKE, 1.0, 1 << 24, K, 1 << 24, FAKE, FAKE, 1, qtype, 0, FAKE, FAKE, 1 << 62, None)
+        assert st == 2 and "2^40" in msg, msg
+        for scheme, name in ((1, "w8a8_static"), (3, "w8a8_dynamic")):
+            need = qlq.linear_workspace_bytes(name, M, K, N, "int8" if qtype == 0 else "fp8_e4m3fn")
+            st, msg = _status(L.qlq_linear, scheme, FAKE, M, K, N, FAKE, FAKE, 3, qtype, 1.0, None, 0, FAKE, FAKE,
+                              need, None)
+            assert st == 1 and "w_scale_numel" in msg, msg
+            st, msg = _status(L.qlq_linear, scheme, FAKE, M, K, N, FAKE, FAKE, N, qtype, 1.0, mis, 0, FAKE, FAKE,
+                              need, None)
+            assert st == 1 and "aligned" in msg, msg
+            st, msg = _status(L.qlq_linear, scheme, FAKE, M, K, N, FAKE, FAKE, N, qtype, 1.0, None, 0, mis, FAKE,
+                              need, None)
+            assert st == 1 and "aligned" in msg, msg
+
+
+def _bf16_positive_finite():
+    import numpy as np
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)            # +denormals .. largest finite
+    return (bits << 16).view(np.float32)
+
+
+def _calibrated_by_definition(s):
+    """s = fp32(a / qmax) for some positive finite bf16 a and qmax in {127, 448}, and s >= 2^-100
+    (brute force over every such a)."""
+    import numpy as np
+    a = _bf16_positive_finite()
+    s = np.float32(s)
+    if not np.isfinite(s) or not s >= np.float32(2.0 ** -100):
+        return False
+    return any(bool(np.any((a / np.float32(q)).astype(np.float32) == s)) for q in (127.0, 448.0))
+
+
+def test_scale_classifier_accepts_exactly_the_calibrated_scales():
+    import numpy as np
+    rng = np.random.default_rng(5)
+    a = _bf16_positive_finite()
+    picks = np.concatenate([a[rng.integers(0, a.size, 300)], a[:5], a[-5:],
+                            np.array([1.0, 3.0, 0.5, 2.0 ** -110, 2.0 ** -90], np.float32)])
+    accepted = rejected = 0
+    for q in (127.0, 448.0):
+        for ai in picks:
+            s = np.float32(ai) / np.float32(q)
+            cand = [s, np.nextafter(s, np.float32(np.inf)), np.nextafter(s, np.float32(0.0)),
+                    np.float32(s * np.float32(1.5))]
+            for c in cand:
+                want = _calibrated_by_definition(c)
+                assert qlq.scale_is_calibrated(float(c)) == want, (float(ai), q, float(c))
+                accepted += want
+                rejected += not want
+    for bad in [0.0, -1.0 / 127, float("inf"), float("nan"), 2.0 ** -101, 0.1, 1e-3]:
+        assert qlq.scale_is_calibrated(bad) == _calibrated_by_definition(np.float32(bad))
+    assert accepted > 500 and rejected > 500
+
+
+def test_plan_hook_reports_the_kernel_families():
+    p = qlq.gemm_plan("w8a16", 1, 2048, 2048, "int8")
+    assert p["kind"] == 0 and p["tile_n"] == 16 and p["waves"] in (4, 8, 16) and p["cfg"] == -1
+    p = qlq.gemm_plan("w8a16", 1024, 2048, 11008, "int8")
+    assert p["kind"] == 2 and p["cfg"] >= 0 and p["tile_m"] in (128, 256)
+    p = qlq.gemm_plan("w8a8_static", 300, 2000, 300, "int8")
+    assert p["kind"] == 1
+    p = qlq.gemm_plan("w8a8_static", 256, 11008, 2048, "int8")
+    assert p["split_k"] > 1 and 0 < p["workspace_bytes"] <= qlq.workspace_bytes("w8a8_static", 256, 11008, 2048, "int8")
+    with pytest.raises(qlq.QlqError):
+        qlq.gemm_plan("w8a16", 0, 64, 64, "int8")
+
+
+def test_requant_parity_shapes_reach_every_plan_of_the_stack_chain():
+    """Every launch plan (kernel family, tile configuration, split or not, waves) that
+    the 3B-scale stack's W8A8 chain takes is also taken by a requantizing-epilogue
+    parity shape, so a planner refit cannot leave a timed plan without an oracle
+    comparison of its code-writing epilogue."""
+    import synth
+    from tests.test_gpu_requant import SHAPES
+
+    def key(p):
+        return p["kind"], p["cfg"], p["split_k"] > 1, p["waves"]
+
+    for qtype in ("int8", "fp8_e4m3fn"):
+        tested = {key(qlq.gemm_plan("w8a8_static", *mkn, qtype)) for mkn in SHAPES}
+        for M in synth.STACK_M:
+            for name, K, N in synth.STACK_PROJS:
+                k = key(qlq.gemm_plan("w8a8_static", M, K, N, qtype))
+                assert k in tested, (qtype, M, name, k)

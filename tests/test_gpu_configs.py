@@ -50,10 +50,34 @@ def test_single_gemm_workload(name):
 STACK_LAYERS = 2
 
 
+def _e4m3_step(v: np.ndarray) -> np.ndarray:
+    """Spacing of e4m3fn values around |v| (3 mantissa bits; 2^-9 below the normal range)."""
+    a = np.maximum(np.abs(v), 2.0 ** -6)
+    return 2.0 ** (np.floor(np.log2(a)) - 3)
+
+
+def check_requant_codes(cb, c_ref, yb, y_ref, s_next, qtype, what):
+    """Codes of the requantizing epilogue against the oracle's quantize_act_static(y_ref, s_next).
+    INT8 (y bit-exact): identical.  FP8: identical wherever y agrees bit for bit; elsewhere
+    each code decodes to within the output tolerance (over s_next) plus one e4m3 step of
+    y_ref / s_next, i.e. it is the code of a valid y."""
+    if qtype == "int8":
+        assert np.array_equal(cb, c_ref), what
+        return
+    same = yb == y_ref
+    assert np.array_equal(cb[same], c_ref[same]), what
+    yr = bits_to_f64(y_ref)
+    tol = 8e-3 * (np.abs(yr) + np.sqrt(np.mean(yr ** 2))) / np.float64(s_next)
+    target = np.clip(yr / np.float64(s_next), -448.0, 448.0)
+    got = oracle.e4m3fn_decode(cb).astype(np.float64)
+    assert np.all(np.abs(got - target) <= tol + _e4m3_step(target)), what
+
+
 @pytest.mark.parametrize("M", synth.STACK_M)
 @pytest.mark.parametrize("variant", ["int8_w8a16", "fp8_w8a8_static"])
 def test_layer_stack_per_layer(variant, M):
-    """First layers of the 36-layer stack, layer by layer.
+    """First layers of the 36-layer stack, layer by layer, through the calls the
+    timed chains make.
 
     The oracle runs its own chain from the seeded inputs; every GPU call gets the
     oracle chain's input for that layer (copied to the device), so each call is
@@ -61,31 +85,47 @@ def test_layer_stack_per_layer(variant, M):
     each round to bf16 after every GEMM drift apart by about one bf16 ulp per
     element within a few layers, so chained outputs are not comparable at the
     per-GEMM tolerance.)
+
+    FP8 W8A8: the chain's input is quantized once (quantize_act_static, codes
+    bit-exact); every layer then runs the requantizing GEMM with the next layer's
+    calibrated scale, and its bf16 output and the codes it writes are compared
+    with the oracle (y within tolerance, codes under the validity rule).  Each
+    layer's input codes are the oracle's.
     """
     print(f"stack per-layer {variant} M={M}", flush=True)
     calib, x = synth.stack_inputs(0, M)
     qtype, gran = ("int8", "per_channel") if variant == "int8_w8a16" else ("fp8_e4m3fn", "per_tensor")
     h_ref, cal_ref = x, calib
+    sx_ref = oracle.calibrate_input_scale(cal_ref, qtype) if variant != "int8_w8a16" else None
     for l in range(STACK_LAYERS):
         for p in range(3):
             w = synth.stack_weight(0, l, p, dev())
             qw = qlq.quantize_weight(w, qtype, gran)
             q_ref, s_ref = oracle.quantize_weight(w.cpu().numpy(), qtype, gran)
+            what = f"{variant} M={M} layer {l} proj {p}"
             if variant == "int8_w8a16":
                 y = qlq.qlinear_w8a16(bf16_to_gpu(h_ref), qw)
                 h_ref = oracle.qlinear_w8a16(h_ref, q_ref, s_ref, qtype)
-            else:
-                # offline calibration through the bf16-dequant chain (oracle's chain)
-                sx_ref = oracle.calibrate_input_scale(cal_ref, qtype)
-                sx_gpu = qlq.calibrate_input_scale(bf16_to_gpu(cal_ref), qtype).item()
-                assert np.float32(sx_gpu) == sx_ref, f"layer {l} proj {p} input scale"
-                cal_ref = oracle.qlinear_w8a16(cal_ref, q_ref, s_ref, qtype)
-                xq_ref = oracle.quantize_act_static(h_ref, sx_ref, qtype)
-                xq = qlq.quantize_act_static(bf16_to_gpu(h_ref), float(sx_ref), qtype)
-                assert np.array_equal(codes(xq), xq_ref.view(np.uint8))
-                y = qlq.qlinear_w8a8_static(xq, float(sx_ref), qw, "bf16")
-                h_ref = oracle.qlinear_w8a8_static(xq_ref, sx_ref, q_ref, s_ref, qtype)
-            check_close(bits_to_f64(bf16_bits(y)), bits_to_f64(h_ref), f"{variant} M={M} layer {l} proj {p}")
+                check_close(bits_to_f64(bf16_bits(y)), bits_to_f64(h_ref), what)
+                continue
+            # offline calibration through the bf16-dequant chain (oracle's chain); the GPU
+            # calibration gives the same scale
+            sx_gpu = qlq.calibrate_input_scale(bf16_to_gpu(cal_ref), qtype).item()
+            assert np.float32(sx_gpu) == sx_ref, f"{what}: input scale"
+            cal_ref = oracle.qlinear_w8a16(cal_ref, q_ref, s_ref, qtype)
+            s_next = oracle.calibrate_input_scale(cal_ref, qtype)
+            xq_ref = oracle.quantize_act_static(h_ref, sx_ref, qtype)
+            if l == 0 and p == 0:                      # the chain's one separate quantization pass
+                xq0 = qlq.quantize_act_static(bf16_to_gpu(h_ref), float(sx_ref), qtype)
+                assert np.array_equal(codes(xq0), xq_ref.view(np.uint8)), what
+            xq = torch.from_numpy(xq_ref.view(np.uint8).copy()).to(dev())
+            y, c = qlq.qlinear_w8a8_static_requant(xq, float(sx_ref), qw, float(s_next))
+            h_ref = oracle.qlinear_w8a8_static(xq_ref, sx_ref, q_ref, s_ref, qtype)
+            yb = bf16_bits(y)
+            check_close(bits_to_f64(yb), bits_to_f64(h_ref), what)
+            c_ref = oracle.quantize_act_static(h_ref, s_next, qtype).view(np.uint8)
+            check_requant_codes(codes(c), c_ref, yb, h_ref, s_next, qtype, what)
+            sx_ref = s_next
 
 
 @pytest.mark.parametrize("M", [16, 1024])

@@ -29,7 +29,10 @@ QTYPES = ["int8", "fp8_e4m3fn"]
 # split-K)
 SHAPES = [(1, 1, 1), (1, 2048, 1024), (1, 2048, 2048), (3, 100, 37), (16, 640, 200), (16, 11008, 128),
           (64, 128, 4096), (130, 4096, 96), (255, 1024, 136), (257, 320, 250), (256, 11008, 256),
-          (1024, 2048, 1024), (130, 1000, 96), (40, 200, 64), (300, 2000, 300)]
+          (1024, 2048, 1024), (130, 1000, 96), (40, 200, 64), (300, 2000, 300),
+          # plans of the 3B-scale stack's chain: small-M without split (4 waves) and with split
+          # (8 / 16 waves), and the 256x192 tile the up projection takes at M = 1024
+          (1, 2048, 11008), (16, 11008, 2048), (768, 512, 11008)]
 
 
 def _e4m3_step(v: np.ndarray) -> np.ndarray:

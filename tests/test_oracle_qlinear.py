@@ -114,6 +114,26 @@ def test_int8_relative_error_matches_uniform_noise_law():
     assert 0.005 < rel < 0.0095 * 1.5 and cos > 0.9998
 
 
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_reconstruction_error_closed_form(qtype):
+    """Rows built from Pythagorean pairs have known cosines: dequant (3, 4) against
+    W (4, 3) has cosine 24/25, (5, 12) against (12, 5) has 120/169; a zero row and
+    an exact row have cosine 1.  The minimum over rows is 120/169 and the relative
+    L2 error is sqrt(100 / 243).  A column-wise cosine (0.976), a mean over rows
+    (0.917) or scales applied along the wrong axis give other values."""
+    W = np.array([[4, 3, 0, 0], [12, 5, 0, 0], [0, 0, 0, 0], [0, 0, 7, 0]], np.float32)
+    q = np.array([[6, 8, 0, 0], [5, 12, 0, 0], [0, 0, 0, 0], [0, 0, 7, 0]], np.float32)
+    s = np.array([0.5, 1.0, 1.0, 1.0], np.float32)          # row 0 dequantizes to (3, 4)
+    codes = q.astype(np.int8) if qtype == "int8" else oracle.e4m3fn_encode_sat(q)
+    assert np.array_equal(oracle.e4m3fn_decode(codes), q) if qtype != "int8" else True
+    rel, cos = oracle.reconstruction_error(W, codes, s, qtype)
+    assert cos == pytest.approx(120 / 169, abs=1e-15)
+    assert rel == pytest.approx(np.sqrt(100 / 243), abs=1e-15)
+    # a per-tensor scale broadcasts over every row
+    rel1, cos1 = oracle.reconstruction_error(W[1:], codes[1:], np.array([1.0], np.float32), qtype)
+    assert cos1 == pytest.approx(120 / 169, abs=1e-15) and rel1 == pytest.approx(np.sqrt(98 / 218), abs=1e-15)
+
+
 def test_integer_weights_scale_one_int8():
     rng = np.random.default_rng(9)
     W = rng.integers(-127, 128, size=(16, 40)).astype(np.float32)

@@ -59,6 +59,8 @@ _SIGNATURES = {
                               _c.c_int64, _c.c_int, _c.c_float, _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p,
                               _c.c_size_t, _c.c_void_p]),
     "qlq_linear_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "qlq_gemm_plan": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p]),
+    "qlq_scale_is_calibrated": (_c.c_int, [_c.c_float]),
     "qlq_status_string": (_c.c_char_p, [_c.c_int]),
     "qlq_last_error": (_c.c_char_p, []),
     "qlq_version": (_c.c_char_p, []),
@@ -137,6 +139,24 @@ def packed_weight_bytes(N: int, K: int) -> int:
 
 def workspace_bytes(scheme: str, M: int, K: int, N: int, qtype: str) -> int:
     return int(lib().qlq_workspace_bytes(SCHEMES[scheme], M, K, N, _qtype(qtype)))
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("cfg", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+
+
+def gemm_plan(scheme: str, M: int, K: int, N: int, qtype: str) -> dict:
+    """The launch plan a GEMM call takes for these sizes (test hook; host only)."""
+    info = _PlanInfo()
+    _check(lib().qlq_gemm_plan(SCHEMES[scheme], M, K, N, _qtype(qtype), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
+
+
+def scale_is_calibrated(s: float) -> bool:
+    """Whether the quantizers take the refined-reciprocal division for scale s (test hook)."""
+    return bool(lib().qlq_scale_is_calibrated(float(s)))
 
 
 _workspaces: dict = {}

@@ -332,12 +332,24 @@ qlq_status qlq_quantize_act_dynamic(const void* x_bf16, int64_t M, int64_t K, ql
                     "quantize_act_dynamic");
 }
 
+// A GEMM call after validation: its plan and kernel arguments.  Preparing runs
+// every check and has no side effect; launching enqueues the kernels.  Calls that
+// enqueue more than one kernel prepare everything before the first launch, so a
+// rejected call leaves the stream (or a graph being captured) untouched.
+struct PreparedGemm {
+  int scheme = 0;
+  int qtype = 0;
+  qlq::GemmPlan plan;
+  qlq::GemmArgs args{};
+  const char* what = "";
+};
+
 // x: bf16 for W8A16, codes for W8A8.
-static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int64_t N, const void* wq_packed,
-                           const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
-                           const float* row_scale, int out_acc, void* y, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream, const char* what,
-                           const void* bias = nullptr, void* y_codes = nullptr, float next_scale = 1.0f) {
+static qlq_status prepare_gemm(PreparedGemm& g, int scheme, const void* x, int64_t M, int64_t K, int64_t N,
+                               const void* wq_packed, const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype,
+                               float input_scale, const float* row_scale, int out_acc, void* y, void* workspace,
+                               size_t workspace_bytes, const char* what, const void* bias = nullptr,
+                               void* y_codes = nullptr, float next_scale = 1.0f) {
   if (!x || !wq_packed || !w_scale || !y) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
   if (qlq_status st = check_dims(M, K, N)) return st;
   if (M * N > kMaxOutputs) return fail(QLQ_ERR_UNSUPPORTED, "M * N above 2^40 outputs is not supported");
@@ -359,7 +371,8 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
-  qlq::GemmArgs a;
+  qlq::GemmArgs& a = g.args;
+  a = qlq::GemmArgs{};
   a.x = x;
   a.w = static_cast<const uint8_t*>(wq_packed);
   a.w_scale = w_scale;
@@ -382,10 +395,31 @@ static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int6
   a.next_scale_rcp = (y_codes && calibrated_scale(next_scale)) ? 1 : 0;
   a.out_acc = out_acc;
   a.fast = fast;
-  hipError_t e = plan.kind == 0   ? qlq::launch_gemm_small(scheme, (int)qtype, plan, a, stream)
-                 : plan.kind == 1 ? qlq::launch_gemm_large(scheme, (int)qtype, plan, a, stream)
-                                  : qlq::launch_gemm_mfma(scheme, (int)qtype, plan, a, stream);
-  return hip_status(e, what);
+  g.scheme = scheme;
+  g.qtype = (int)qtype;
+  g.plan = plan;
+  g.what = what;
+  return QLQ_OK;
+}
+
+static qlq_status launch_gemm(const PreparedGemm& g, hipStream_t stream) {
+  hipError_t e = g.plan.kind == 0   ? qlq::launch_gemm_small(g.scheme, g.qtype, g.plan, g.args, stream)
+                 : g.plan.kind == 1 ? qlq::launch_gemm_large(g.scheme, g.qtype, g.plan, g.args, stream)
+                                    : qlq::launch_gemm_mfma(g.scheme, g.qtype, g.plan, g.args, stream);
+  return hip_status(e, g.what);
+}
+
+static qlq_status run_gemm(int scheme, const void* x, int64_t M, int64_t K, int64_t N, const void* wq_packed,
+                           const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype, float input_scale,
+                           const float* row_scale, int out_acc, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, const char* what,
+                           const void* bias = nullptr, void* y_codes = nullptr, float next_scale = 1.0f) {
+  PreparedGemm g;
+  if (qlq_status st = prepare_gemm(g, scheme, x, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale,
+                                   row_scale, out_acc, y, workspace, workspace_bytes, what, bias, y_codes,
+                                   next_scale))
+    return st;
+  return launch_gemm(g, stream);
 }
 
 qlq_status qlq_qlinear_w8a16(const void* x_bf16, int64_t M, int64_t K, int64_t N, const void* wq_packed,
@@ -449,12 +483,16 @@ qlq_status qlq_qlinear_w8a8_static_fused(const void* x_bf16, float input_scale, 
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   void* xq = static_cast<uint8_t*>(workspace) + off;
+  PreparedGemm g;
+  if (qlq_status st = prepare_gemm(g, qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype,
+                                   input_scale, nullptr, out == QLQ_OUT_ACC ? 1 : 0, y, workspace, off,
+                                   "qlinear_w8a8_static_fused"))
+    return st;
   if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream,
-                                          calibrated_scale(input_scale)),
+                                                       calibrated_scale(input_scale)),
                                  "qlinear_w8a8_static_fused"))
     return st;
-  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, input_scale, nullptr,
-                  out == QLQ_OUT_ACC ? 1 : 0, y, workspace, off, stream, "qlinear_w8a8_static_fused");
+  return launch_gemm(g, stream);
 }
 
 qlq_status qlq_qlinear_w8a8_dynamic(const void* xq, const float* x_scale, int64_t M, int64_t K, int64_t N,
@@ -540,21 +578,45 @@ qlq_status qlq_linear(qlq_scheme scheme, const void* x_bf16, int64_t M, int64_t 
   if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const size_t off = linear_codes_offset(M, K, N, (int)qtype);
   void* xq = static_cast<uint8_t*>(workspace) + off;
-  const float* rows = nullptr;
-  if (scheme == QLQ_SCHEME_W8A8_STATIC) {
-    if (qlq_status st = hip_status(qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream,
-                                          calibrated_scale(input_scale)), "linear"))
-      return st;
-  } else {
-    float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(xq) + ((size_t)M * (size_t)K + 255) / 256 * 256);
-    if (qlq_status st = hip_status(qlq::launch_quant_act_dynamic(x_bf16, (int)M, (int)K, (int)qtype, xq, xs, stream),
-                                   "linear"))
-      return st;
-    rows = xs;
-  }
-  return run_gemm(qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype,
-                  scheme == QLQ_SCHEME_W8A8_STATIC ? input_scale : 1.0f, rows, 0, y_bf16, workspace, off, stream,
-                  "linear", bias_bf16);
+  float* xs = scheme == QLQ_SCHEME_W8A8_DYNAMIC
+                  ? reinterpret_cast<float*>(static_cast<uint8_t*>(xq) + ((size_t)M * (size_t)K + 255) / 256 * 256)
+                  : nullptr;
+  PreparedGemm g;
+  if (qlq_status st = prepare_gemm(g, qlq::kW8A8, xq, M, K, N, wq_packed, w_scale, w_scale_numel, qtype,
+                                   scheme == QLQ_SCHEME_W8A8_STATIC ? input_scale : 1.0f, xs, 0, y_bf16, workspace,
+                                   off, "linear", bias_bf16))
+    return st;
+  hipError_t e = scheme == QLQ_SCHEME_W8A8_STATIC
+                     ? qlq::launch_quant_act(x_bf16, M * K, input_scale, (int)qtype, xq, stream,
+                                             calibrated_scale(input_scale))
+                     : qlq::launch_quant_act_dynamic(x_bf16, (int)M, (int)K, (int)qtype, xq, xs, stream);
+  if (qlq_status st = hip_status(e, "linear")) return st;
+  return launch_gemm(g, stream);
+}
+
+// ------------------------------------------------------------------ test hooks
+
+int qlq_scale_is_calibrated(float s) { return calibrated_scale(s) ? 1 : 0; }
+
+qlq_status qlq_gemm_plan(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq_qtype qtype,
+                         qlq_plan_info* info) {
+  if (!info) return fail(QLQ_ERR_INVALID_ARG, "null pointer");
+  if (qlq_status st = check_dims(M, K, N)) return st;
+  if (qlq_status st = check_qtype(qtype)) return st;
+  if (scheme != QLQ_SCHEME_W8A16 && scheme != QLQ_SCHEME_W8A8_STATIC && scheme != QLQ_SCHEME_W8A8_DYNAMIC &&
+      scheme != QLQ_SCHEME_W8A8_STATIC_FUSED)
+    return fail(QLQ_ERR_UNSUPPORTED, "unknown scheme %d", (int)scheme);
+  const int sch = scheme == QLQ_SCHEME_W8A16 ? qlq::kW8A16 : qlq::kW8A8;
+  const qlq::GemmPlan p = qlq::plan_gemm(sch, (int)qtype, M, K, N, K % 64 == 0);
+  info->kind = p.kind;
+  info->cfg = p.kind == 2 ? p.cfg : -1;
+  info->split_k = p.S;
+  info->tile_m = p.kind == 0 ? 16 : p.BM;
+  info->tile_n = p.kind == 0 ? 16 : p.BN;
+  info->waves = p.kind == 0 ? p.waves : 0;
+  info->grid = p.grid;
+  info->workspace_bytes = (int64_t)p.ws_bytes;
+  return ok();
 }
 
 }  // extern "C"
