@@ -153,6 +153,23 @@ qlq_status qlq_qlinear_w8a16(const void* x_bf16, int64_t M, int64_t K, int64_t N
                              qlq_qtype qtype, void* y_bf16,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Allocation-free W8A16, for callers that cannot allocate or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and result as qlq_qlinear_w8a16, without the workspace:
+ * the split-K partial sums and arrival counters live in a device array inside the
+ * library (QLQ_NOALLOC_MAX_SCRATCH_BYTES, one copy per GPU, held until the process
+ * ends).  The call allocates and frees nothing; its first call on a device looks up
+ * that device's copy of the array.  The counters a call uses are cleared by a small
+ * kernel before its GEMM, on `stream`.  Every call on one GPU shares that GPU's array,
+ * so calls that may overlap in time on one GPU (different streams) race; serialize
+ * them or use qlq_qlinear_w8a16 with separate workspaces.  A plan that needs more
+ * scratch than the array holds is rejected with QLQ_ERR_INVALID_ARG (the 3B-scale
+ * stack's shapes need at most 32 MiB + 4 KiB up to M = 1024). */
+#define QLQ_NOALLOC_MAX_SCRATCH_BYTES ((size_t)32 * 1024 * 1024 + 4096)
+qlq_status qlq_qlinear_w8a16_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t N,
+                                     const void* wq_packed, const float* w_scale, int64_t w_scale_numel,
+                                     qlq_qtype qtype, void* y_bf16, hipStream_t stream);
+
 /* W8A8 static quantized linear on codes from qlq_quantize_act_static:
  *   acc[m,n] = sum_k xq[m,k] * q[n,k]   (INT8: exact int32; FP8: fp32)
  *   y[m,n]   = bf16( fp32(acc[m,n]) * fp32(input_scale * s[n]) )

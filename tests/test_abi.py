@@ -329,3 +329,17 @@ def test_requant_parity_shapes_reach_every_plan_of_the_stack_chain():
             for name, K, N in synth.STACK_PROJS:
                 k = key(qlq.gemm_plan("w8a8_static", M, K, N, qtype))
                 assert k in tested, (qtype, M, name, k)
+
+
+def test_noalloc_call_validates_on_the_host():
+    """The allocation-free W8A16 call checks its arguments, and that its plan fits the
+    library's scratch array, before it looks up a device (no GPU here)."""
+    L = qlq.lib()
+    f = L.qlq_qlinear_w8a16_noalloc
+    st, msg = _status(f, None, 1, 64, 16, FAKE, FAKE, 16, 0, FAKE, None)
+    assert st == 1 and "null" in msg
+    st, msg = _status(f, FAKE, 1, 64, 16, FAKE, FAKE, 3, 0, FAKE, None)
+    assert st == 1 and "w_scale_numel" in msg
+    assert qlq.gemm_plan("w8a16", 2048, 11008, 2048, "int8")["workspace_bytes"] > 32 * 1024 * 1024 + 4096
+    st, msg = _status(f, FAKE, 2048, 11008, 2048, FAKE, FAKE, 2048, 0, FAKE, None)
+    assert st == 1 and "scratch" in msg

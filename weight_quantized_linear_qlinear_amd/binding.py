@@ -36,6 +36,8 @@ _SIGNATURES = {
                                            _c.c_void_p, _c.c_void_p]),
     "qlq_qlinear_w8a16": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                      _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "qlq_qlinear_w8a16_noalloc": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p,
+                                             _c.c_void_p, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p]),
     "qlq_qlinear_w8a8_static": (_c.c_int, [_c.c_void_p, _c.c_float, _c.c_int64, _c.c_int64, _c.c_int64,
                                            _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int,
                                            _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -269,6 +271,19 @@ def qlinear_w8a16(x: torch.Tensor, qw: QuantizedWeight, out: torch.Tensor | None
     _check(lib().qlq_qlinear_w8a16(_ptr(x), M, qw.K, qw.N, _ptr(qw.packed), _ptr(qw.scale), qw.scale.numel(),
                                    _qtype(qw.qtype), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(x.device)))
+    return out
+
+
+def qlinear_w8a16_noalloc(x: torch.Tensor, qw: QuantizedWeight, out: torch.Tensor) -> torch.Tensor:
+    """qlinear_w8a16 without a workspace (split-K scratch inside the library); out is required."""
+    _require_gpu(x, out)
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.shape[1] != qw.K:
+        raise ValueError(f"x must be bf16 [M, {qw.K}]")
+    M = x.shape[0]
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, qw.N):
+        raise ValueError(f"out must be bf16 [{M}, {qw.N}]")
+    _check(lib().qlq_qlinear_w8a16_noalloc(_ptr(x), M, qw.K, qw.N, _ptr(qw.packed), _ptr(qw.scale),
+                                           qw.scale.numel(), _qtype(qw.qtype), _ptr(out), _stream(x.device)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "qlq_launch.h"
@@ -344,6 +345,28 @@ struct PreparedGemm {
   const char* what = "";
 };
 
+// Points a prepared call's split-K counters and partials into `workspace` (checks
+// its size and alignment; nothing when the plan needs no workspace).
+static qlq_status bind_workspace(PreparedGemm& g, void* workspace, size_t workspace_bytes) {
+  const qlq::GemmPlan& plan = g.plan;
+  qlq::GemmArgs& a = g.args;
+  a.counters = nullptr;
+  a.partials = nullptr;
+  a.partials_bytes = 0u;
+  if (plan.ws_bytes == 0) return QLQ_OK;
+  if (!workspace || workspace_bytes < plan.ws_bytes)
+    return fail(QLQ_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_counter_bytes);
+  a.partials_bytes = (uint32_t)(plan.ws_bytes - plan.ws_counter_bytes);
+  return QLQ_OK;
+}
+
+// Passed as prepare_gemm's workspace to leave the binding to a later bind_workspace.
+static void* const kWorkspaceLater = reinterpret_cast<void*>(~uintptr_t{0});
+
 // x: bf16 for W8A16, codes for W8A8.
 static qlq_status prepare_gemm(PreparedGemm& g, int scheme, const void* x, int64_t M, int64_t K, int64_t N,
                                const void* wq_packed, const float* w_scale, int64_t w_scale_numel, qlq_qtype qtype,
@@ -363,14 +386,8 @@ static qlq_status prepare_gemm(PreparedGemm& g, int scheme, const void* x, int64
     return fail(QLQ_ERR_INVALID_ARG, "misaligned pointer");
   const bool fast = (K % 64 == 0) && aligned(x, 16);
   qlq::GemmPlan plan = qlq::plan_gemm(scheme, (int)qtype, M, K, N, fast);
-  if (plan.ws_bytes > 0) {
-    if (plan.ws_bytes - plan.ws_counter_bytes >= ((size_t)1 << 31))
-      return fail(QLQ_ERR_UNSUPPORTED, "split-K partials above 2 GiB");
-    if (!workspace || workspace_bytes < plan.ws_bytes)
-      return fail(QLQ_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", plan.ws_bytes,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 256)) return fail(QLQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  }
+  if (plan.ws_bytes > 0 && plan.ws_bytes - plan.ws_counter_bytes >= ((size_t)1 << 31))
+    return fail(QLQ_ERR_UNSUPPORTED, "split-K partials above 2 GiB");
   qlq::GemmArgs& a = g.args;
   a = qlq::GemmArgs{};
   a.x = x;
@@ -378,10 +395,6 @@ static qlq_status prepare_gemm(PreparedGemm& g, int scheme, const void* x, int64
   a.w_scale = w_scale;
   a.scale_per_tensor = w_scale_numel == 1 ? 1 : 0;
   a.y = y;
-  a.counters = plan.ws_bytes ? static_cast<uint32_t*>(workspace) : nullptr;
-  a.partials = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_counter_bytes)
-                             : nullptr;
-  a.partials_bytes = plan.ws_bytes ? (uint32_t)(plan.ws_bytes - plan.ws_counter_bytes) : 0u;
   a.M = (int)M;
   a.K = (int)K;
   a.N = (int)N;
@@ -399,7 +412,8 @@ static qlq_status prepare_gemm(PreparedGemm& g, int scheme, const void* x, int64
   g.qtype = (int)qtype;
   g.plan = plan;
   g.what = what;
-  return QLQ_OK;
+  if (workspace == kWorkspaceLater) return QLQ_OK;
+  return bind_workspace(g, workspace, workspace_bytes);
 }
 
 static qlq_status launch_gemm(const PreparedGemm& g, hipStream_t stream) {
@@ -620,3 +634,71 @@ qlq_status qlq_gemm_plan(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------- allocation-free W8A16
+// For callers that cannot allocate (HIP graph capture, tight serving loops): the
+// split-K counters and partials live in this file-scope device array, one copy per
+// GPU, instead of a caller's workspace.  Host code uses the array only through the
+// device address hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) uint8_t scratch[QLQ_NOALLOC_MAX_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = QLQ_NOALLOC_MAX_SCRATCH_BYTES;
+static_assert(kScratchBytes > kCounterBytes, "scratch holds the counter region and partials");
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+qlq_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (qlq_status st = hip_status(hipGetDevice(&dev), "qlinear_w8a16_noalloc")) return st;
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(QLQ_ERR_UNSUPPORTED, "qlinear_w8a16_noalloc: device index %d above %d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (qlq_status st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "qlinear_w8a16_noalloc: scratch"))
+      return st;
+    if (!p || !aligned(p, 256)) return fail(QLQ_ERR_HIP, "qlinear_w8a16_noalloc: scratch address unusable");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLQ_OK;
+}
+
+// Zeroes n arrival counters (a kernel, not a memset node, so the call stays capturable).
+__global__ void clear_counters_kernel(uint32_t* c, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" qlq_status qlq_qlinear_w8a16_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t N,
+                                                const void* wq_packed, const float* w_scale,
+                                                int64_t w_scale_numel, qlq_qtype qtype, void* y_bf16,
+                                                hipStream_t stream) {
+  PreparedGemm g;
+  if (qlq_status st = prepare_gemm(g, qlq::kW8A16, x_bf16, M, K, N, wq_packed, w_scale, w_scale_numel, qtype, 1.0f,
+                                   nullptr, 0, y_bf16, kWorkspaceLater, 0, "qlinear_w8a16_noalloc"))
+    return st;
+  if (g.plan.ws_bytes > kScratchBytes)
+    return fail(QLQ_ERR_INVALID_ARG,
+                "qlinear_w8a16_noalloc: this plan needs %zu bytes of split-K scratch, above the %zu the "
+                "allocation-free call holds (use qlq_qlinear_w8a16 with a workspace)",
+                g.plan.ws_bytes, kScratchBytes);
+  if (g.plan.ws_bytes > 0) {
+    void* p = nullptr;
+    if (qlq_status st = scratch_of_current_device(&p)) return st;
+    if (qlq_status st = bind_workspace(g, p, kScratchBytes)) return st;
+    // The array keeps the last call's contents: the counters this plan uses start at zero.
+    const int n = g.plan.tiles;
+    clear_counters_kernel<<<(n + 255) / 256, 256, 0, stream>>>(g.args.counters, n);
+    if (qlq_status st = hip_status(hipGetLastError(), "qlinear_w8a16_noalloc")) return st;
+  }
+  return launch_gemm(g, stream);
+}
