@@ -311,6 +311,51 @@ def kv_rows(qlq, torch, dev, Ts, steps, warmup):
     return res
 
 
+BUCKET_M = (1, 5, 13, 100, 300)     # batch sizes that are not buckets (except 1), padded to 1, 8, 16, 128, 512
+
+
+def bucket_rows(qlq, synth, torch, dev, qi, L, steps, warmup):
+    """The INT8 W8A16 stack through decode-batch graph buckets (GraphBuckets): one captured
+    graph per bucket size (1, 2, 4, ..., 512); a batch of M rows is copied into its
+    bucket's input (pad rows zeroed) and the bucket's graph is replayed."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    mids = {}
+
+    def fn(x, y):
+        b = x.shape[0]
+        h = x
+        for l in range(L):
+            for p, (_, K, N) in enumerate(synth.STACK_PROJS):
+                last = l == L - 1 and p == len(synth.STACK_PROJS) - 1
+                out = y if last else mids.setdefault((b, l % 2, p), torch.empty((b, N), dtype=torch.bfloat16,
+                                                                                  device=dev))
+                qlq.qlinear_w8a16(h, qi[l][p], out=out, workspace=ws)
+                h = out
+
+    gb = qlq.GraphBuckets(fn, synth.HIDDEN, synth.HIDDEN, device=dev)
+    res = {}
+    cur = torch.cuda.current_stream()
+    for M in BUCKET_M:
+        x = torch.randn((M, synth.HIDDEN), device=dev).to(torch.bfloat16)
+        for _ in range(warmup):
+            gb(x)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(steps):
+            gb(x)
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        b = gb.bucket_for(M)
+        flops = sum(2 * M * N * K for _, K, N in synth.STACK_PROJS) * L
+        res[f"bucketed_int8_w8a16/M={M}"] = {"bucket": b, "us_per_stack": round(us, 2),
+                                              "us_per_gemm": round(us / (3 * L), 3),
+                                              "tflops_real_rows": round(flops / us / 1e6, 2)}
+    return res
+
+
 def cpu_baseline(seed, layers_w, sx):
     """Time the oracle on layer 0 of the stack (both variants, every M)."""
     import numpy as np
@@ -521,6 +566,7 @@ def main():
     out_cases, tot_flops = figures(VARIANTS, groups)
     next_cases_out, _ = figures(NEXT_VARIANTS)
     next_cases_out.update(kv_rows(qlq, torch, dev, KV_TOKENS, args.steps, args.warmup))
+    next_cases_out.update(bucket_rows(qlq, synth, torch, dev, qi, L, args.steps, args.warmup))
     single = single_gemm_rows(qlq, synth, torch, dev)
     out_cases.update(single)
     # dominant kernel: the (variant, kernel family) group with the most time
@@ -557,9 +603,10 @@ def main():
                        "layers": L, "M": list(Ms), "variants": [v[0] for v in VARIANTS],
                        "gemms_per_step": 3 * L * len(cases)},
             "cases": out_cases, "roofline": roof,
-            "next_rows": {"note": "INT8 W8A8 with dynamic per-token activation scales on the same stack, and "
-                                  "the mixed K-int8/V-FP8 KV-cache codec (28 layers x 4 KV heads x 128); "
-                                  "timed after the step, not part of value or ms_per_step",
+            "next_rows": {"note": "INT8 W8A8 with dynamic per-token activation scales on the same stack, the "
+                                  "routed Linear, the mixed K-int8/V-FP8 KV-cache codec (28 layers x 4 KV heads "
+                                  "x 128), and the INT8 W8A16 stack through decode-batch graph buckets (M padded "
+                                  "to 1, 2, 4, ..., 512); timed after the step, not part of value or ms_per_step",
                           "cases": next_cases_out}}
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)

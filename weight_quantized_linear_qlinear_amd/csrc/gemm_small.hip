@@ -220,9 +220,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
     const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
     store_partial(part, ((int64_t)s * a.NT + nt) * 64 + lane, tot);
     wait_stores_performed();
+    // The fences pin the order at the compiler level too: partial stores before the
+    // arrival, partial loads after it (at workgroup scope they add no cache maintenance).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     uint32_t prev = 0;
     if (lane == 0) prev = arrive(&a.counters[nt]);
     prev = __shfl(prev, 0, 64);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (prev != (uint32_t)(S - 1)) return;
     // slices summed in order 0..S-1, whichever workgroup arrived last
     if constexpr (T::kIntAcc) {
