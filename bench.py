@@ -113,8 +113,10 @@ def kernel_sources_hash():
 
 
 def profiled_traffic(family):
-    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE profile, or None when the
-    profile is for another kernel family or the kernels changed since it was taken."""
+    """L2<->fabric bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a device copy of known size) from the
+    committed counter profile, or None when the profile is for another kernel family or the kernels changed
+    since it was taken.  The 256 MB last-level cache can serve these requests, so they bound HBM bytes from
+    above."""
     if family != ("int8_w8a16", "large") or not os.path.exists(TRAFFIC_PROFILE):
         return None
     kv = {}
@@ -125,7 +127,7 @@ def profiled_traffic(family):
         kv[k.strip()] = v.strip()
     if kv.get("sources_sha256") != kernel_sources_hash():
         return None
-    return int(float(kv["hbm_bytes_per_launch"]))
+    return int(float(kv["fabric_bytes_per_launch"]))
 
 
 def build_stack(qlq, synth, torch, dev, seed, layers):
@@ -400,6 +402,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=36, help="decoder layers in the stack (36 = the pages' config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step only: skip next_rows and the single-GEMM workloads (short profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run one 256 MiB device copy (known HBM bytes) so that "
                          "profiler byte counters can be scaled")
@@ -488,7 +492,7 @@ def main():
 
     # capture one graph per (variant, M)
     cases = [(v[0], M) for v in VARIANTS for M in Ms]
-    next_cases = [(v[0], M) for v in NEXT_VARIANTS for M in Ms]
+    next_cases = [] if args.only_step else [(v[0], M) for v in NEXT_VARIANTS for M in Ms]
     graphs = {}
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -528,10 +532,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     # the widened rows, timed after the main region (not part of the step)
-    for _ in range(args.warmup):
-        step(False, next_cases)
-    for _ in range(args.steps):
-        step(True, next_cases)
+    if not args.only_step:
+        for _ in range(args.warmup):
+            step(False, next_cases)
+        for _ in range(args.steps):
+            step(True, next_cases)
     torch.cuda.synchronize()
 
     # per-case figures
@@ -564,11 +569,12 @@ def main():
 
     groups = {}
     out_cases, tot_flops = figures(VARIANTS, groups)
-    next_cases_out, _ = figures(NEXT_VARIANTS)
-    next_cases_out.update(kv_rows(qlq, torch, dev, KV_TOKENS, args.steps, args.warmup))
-    next_cases_out.update(bucket_rows(qlq, synth, torch, dev, qi, L, args.steps, args.warmup))
-    single = single_gemm_rows(qlq, synth, torch, dev)
-    out_cases.update(single)
+    next_cases_out = {}
+    if not args.only_step:
+        next_cases_out, _ = figures(NEXT_VARIANTS)
+        next_cases_out.update(kv_rows(qlq, torch, dev, KV_TOKENS, args.steps, args.warmup))
+        next_cases_out.update(bucket_rows(qlq, synth, torch, dev, qi, L, args.steps, args.warmup))
+        out_cases.update(single_gemm_rows(qlq, synth, torch, dev))
     # dominant kernel: the (variant, kernel family) group with the most time
     fam, g = max(groups.items(), key=lambda kv: kv[1]["us"])
     avg_us = g["us"] / g["launches"]
@@ -583,6 +589,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 3)
     roof["traffic"] = profiled_traffic(fam)
+    roof["traffic_note"] = ("bytes between the L2s and the fabric per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "scaled by a 256 MiB device copy); the MALL can serve them, so an upper bound on HBM "
+                            "bytes; profiles/traffic_gemm_mfma_int8_w8a16_stack.txt")
     roof["algorithmic_bytes_per_launch"] = int(g["bytes"] / g["launches"])
     kernel_name = {("int8_w8a16", "large"): "gemm_mfma_kernel<int8, W8A16, *> (M=256 and M=1024 launches)",
                    ("int8_w8a16", "small"): "gemm_small_kernel<int8, W8A16> (M=1 and M=16 launches)",

@@ -1,0 +1,170 @@
+"""Summaries of rocprofv3 CSV output for the library's kernels.
+
+    python -m weight_quantized_linear_qlinear_amd.profile_summary kernels TRACE.csv [--top N]
+    python -m weight_quantized_linear_qlinear_amd.profile_summary mfma COUNTERS.csv AGENT_INFO.csv [--match RE]
+    python -m weight_quantized_linear_qlinear_amd.profile_summary traffic FETCH.csv WRITE.csv [--match RE]
+
+`kernels` reads a `--kernel-trace` CSV and prints, per kernel and launch size
+(workgroups), the call count and the duration's mean, p10, p50, p90, min and max.
+
+`mfma` reads a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE ...` CSV and prints per
+kernel and launch size the MFMA utilisation: the matrix-pipe busy cycles over all
+SIMDs divided by the SIMD count times the GPU-active cycles of one XCD
+(GRBM_GUI_ACTIVE is summed over the XCDs), plus the MFMA FLOPs the MOPS counters
+report when they were collected.
+
+`traffic` reads one FETCH_SIZE and one WRITE_SIZE run (KiB per dispatch) and prints
+per kernel and launch size the bytes between the L2s and the fabric (the 256 MB
+last-level cache can serve them, so they are an upper bound on HBM bytes, not HBM
+bytes), scaled by what the same counters read for the largest device-to-device
+copy in the run (bytes known: it reads and writes its size).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import re
+import sys
+
+import numpy as np
+
+
+def short_name(name: str) -> str:
+    """qlq kernels without namespaces and argument lists; others truncated."""
+    n = name.replace("void ", "").replace("qlq::(anonymous namespace)::", "").replace("qlq::", "")
+    if "(" in n and n.index("(") > 0 and n.startswith(("gemm", "quant", "pack", "absmax", "finalize", "kv_", "zero",
+                                                        "unpack", "clear")):
+        n = n[:n.index("(")]
+    return n if len(n) <= 110 else n[:107] + "..."
+
+
+def _wgs(grid: int, wg: int) -> int:
+    return grid // wg if wg else grid
+
+
+def kernels(path: str, top: int):
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        key = (short_name(r["Kernel_Name"]), _wgs(int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])),
+               int(r["Workgroup_Size_X"]))
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
+    print("# kernel | workgroups x threads | calls | mean us | p10 | p50 | p90 | min | max | % of GPU time")
+    for (name, wgs, wg), d in rows:
+        a = np.array(d)
+        print(f"{name} | {wgs} x {wg} | {a.size} | {a.mean():.2f} | {np.percentile(a, 10):.2f} | "
+              f"{np.percentile(a, 50):.2f} | {np.percentile(a, 90):.2f} | {a.min():.2f} | {a.max():.2f} | "
+              f"{100 * a.sum() / total:.2f}")
+
+
+def _pivot(path: str, match: str | None):
+    disp = collections.defaultdict(dict)
+    rx = re.compile(match) if match else None
+    for r in csv.DictReader(open(path)):
+        if rx and not rx.search(r["Kernel_Name"]):
+            continue
+        d = disp[int(r["Dispatch_Id"])]
+        d["name"] = r["Kernel_Name"]
+        d["wgs"] = _wgs(int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+        d["wg"] = int(r["Workgroup_Size"])
+        d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    return disp
+
+
+def _gpu_agent(path: str):
+    for r in csv.DictReader(open(path)):
+        if r.get("Agent_Type") == "GPU":
+            return int(r["Simd_Count"]), int(r["Num_Xcc"])
+    raise SystemExit("no GPU agent in " + path)
+
+
+def mfma(path: str, agent_path: str, match: str | None):
+    simds, xcc = _gpu_agent(agent_path)
+    groups = collections.defaultdict(list)
+    for d in _pivot(path, match).values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or not d.get("GRBM_GUI_ACTIVE"):
+            continue
+        util = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * d["GRBM_GUI_ACTIVE"] / xcc)
+        flops = 512 * sum(d.get(c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                                                   "SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_INSTS_VALU_MFMA_MOPS_F16"))
+        groups[(short_name(d["name"]), d["wgs"], d["wg"])].append((util, flops, d["us"]))
+    print(f"# {simds} SIMDs, {xcc} XCDs; MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / "
+          f"({simds} x GRBM_GUI_ACTIVE / {xcc})")
+    print("# kernel | workgroups x threads | dispatches | MFMA util % (mean) | min | max | MFMA GFLOP per dispatch | "
+          "us per dispatch (under the profiler)")
+    for (name, wgs, wg), v in sorted(groups.items(), key=lambda kv: -sum(x[2] for x in kv[1])):
+        a = np.array(v)
+        print(f"{name} | {wgs} x {wg} | {len(v)} | {100 * a[:, 0].mean():.1f} | {100 * a[:, 0].min():.1f} | "
+              f"{100 * a[:, 0].max():.1f} | {a[:, 1].mean() / 1e9:.3f} | {a[:, 2].mean():.2f}")
+
+
+def traffic(fetch_path: str, write_path: str, match: str | None):
+    fetch = _pivot(fetch_path, None)
+    write = _pivot(write_path, None)
+
+    def calib(disp, counter):
+        cp = [d for d in disp.values() if "copyBuffer" in d["name"] or "copy" in d["name"].lower()]
+        if not cp:
+            raise SystemExit("no copy dispatch to calibrate against (run with the copy calibration)")
+        return max(cp, key=lambda d: d.get(counter, 0.0))
+
+    cf, cw = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
+    copy_bytes = 256 << 20
+    kf = copy_bytes / (cf["FETCH_SIZE"] * 1024)
+    kw = copy_bytes / (cw["WRITE_SIZE"] * 1024)
+    print(f"# calibration: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE {cf['FETCH_SIZE']:.0f} KiB and "
+          f"WRITE_SIZE {cw['WRITE_SIZE']:.0f} KiB: factors {kf:.3f} (fetch), {kw:.3f} (write)")
+    rx = re.compile(match) if match else None
+    groups = collections.defaultdict(lambda: [[], []])
+    for d in fetch.values():
+        if rx and not rx.search(d["name"]):
+            continue
+        groups[(short_name(d["name"]), d["wgs"], d["wg"])][0].append(d["FETCH_SIZE"] * 1024 * kf)
+    for d in write.values():
+        if rx and not rx.search(d["name"]):
+            continue
+        groups[(short_name(d["name"]), d["wgs"], d["wg"])][1].append(d["WRITE_SIZE"] * 1024 * kw)
+    print("# kernel | workgroups x threads | dispatches | fetched MB per dispatch | written MB per dispatch | "
+          "L2<->fabric MB per dispatch")
+    tot_f = tot_w = n_all = 0
+    for (name, wgs, wg), (f, w) in sorted(groups.items(), key=lambda kv: -sum(kv[1][0])):
+        if not f or not w:
+            continue
+        mf, mw = float(np.mean(f)), float(np.mean(w))
+        tot_f += sum(f)
+        tot_w += sum(w)
+        n_all += len(f)
+        print(f"{name} | {wgs} x {wg} | {len(f)} | {mf / 1e6:.2f} | {mw / 1e6:.2f} | {(mf + mw) / 1e6:.2f}")
+    if n_all:
+        print(f"fabric_bytes_per_launch: {(tot_f + tot_w) / n_all:.0f}")
+        print(f"dispatches: {n_all}")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("trace")
+    k.add_argument("--top", type=int, default=40)
+    m = sub.add_parser("mfma")
+    m.add_argument("counters")
+    m.add_argument("agent_info")
+    m.add_argument("--match")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch")
+    t.add_argument("write")
+    t.add_argument("--match")
+    a = ap.parse_args(argv)
+    if a.cmd == "kernels":
+        kernels(a.trace, a.top)
+    elif a.cmd == "mfma":
+        mfma(a.counters, a.agent_info, a.match)
+    else:
+        traffic(a.fetch, a.write, a.match)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
