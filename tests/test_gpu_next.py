@@ -45,7 +45,9 @@ def _check_rows(got_bits, ref_bits, what):
 
 @pytest.mark.parametrize("qtype", QTYPES)
 @pytest.mark.parametrize("MK", [(1, 1), (1, 2048), (4, 7), (16, 2048), (5, 1000), (256, 11008), (1024, 2048),
-                                (3, 8), (64, 4104)])
+                                (3, 8), (64, 4104),
+                                # many rows: a wave per row up to K = 4096, a workgroup per row above
+                                (1030, 4096), (1024, 11008), (1100, 5000)])
 def test_quantize_act_dynamic_bit_exact(qtype, MK):
     M, K = MK
     print(f"act dynamic {qtype} M={M} K={K}", flush=True)
