@@ -27,8 +27,11 @@
  *  - Errors: QLQ_ERR_INVALID_ARG for a null pointer where one is required, a size
  *    below 1, a non-finite or non-positive scale, a scale count that is neither 1
  *    nor N, or a workspace that is too small; QLQ_ERR_UNSUPPORTED for an enum value
- *    the call does not know; QLQ_ERR_HIP when a launch fails.  On error nothing is
- *    enqueued and qlq_last_error() returns a message (thread-local).
+ *    the call does not know; QLQ_ERR_HIP when a launch fails.  Every argument is
+ *    checked before the first kernel of a call is enqueued, so after
+ *    QLQ_ERR_INVALID_ARG or QLQ_ERR_UNSUPPORTED nothing is enqueued; after
+ *    QLQ_ERR_HIP, kernels the same call enqueued before the failed launch may
+ *    still run.  qlq_last_error() returns a message (thread-local).
  *  - Numbers: bf16 and OCP FP8 e4m3fn (1-4-3, bias 7, max 448, no infinities;
  *    not the "fnuz" variant).  Non-finite inputs are not supported.
  */
