@@ -358,8 +358,12 @@ def bucket_rows(qlq, synth, torch, dev, qi, L, steps, warmup):
     return res
 
 
+CPU_SAMPLE_LAYERS = 2
+
+
 def cpu_baseline(seed, layers_w, sx):
-    """Time the oracle on layer 0 of the stack (both variants, every M)."""
+    """Time the oracle on the first CPU_SAMPLE_LAYERS layers of the stack (both variants, every M):
+    about 10 s of host work."""
     import numpy as np
     import oracle
     import synth
@@ -369,27 +373,30 @@ def cpu_baseline(seed, layers_w, sx):
     except Exception:
         threads = os.cpu_count()
     # offline steps (not timed): the oracle's own quantized weights
-    w_host = [w.cpu().numpy() for w in layers_w]
-    qi = [oracle.quantize_weight(w, "int8", "per_channel") for w in w_host]
-    qf = [oracle.quantize_weight(w, "fp8_e4m3fn", "per_tensor") for w in w_host]
+    w_host = [[w.cpu().numpy() for w in lw] for lw in layers_w]
+    qi = [[oracle.quantize_weight(w, "int8", "per_channel") for w in lw] for lw in w_host]
+    qf = [[oracle.quantize_weight(w, "fp8_e4m3fn", "per_tensor") for w in lw] for lw in w_host]
     flops = 0
     t0 = time.perf_counter()
     for M in synth.STACK_M:
         _, x = synth.stack_inputs(seed, M)
         h = x
-        for p, (_, K, N) in enumerate(synth.STACK_PROJS):
-            h = oracle.qlinear_w8a16(h, qi[p][0], qi[p][1], "int8")
-            flops += 2 * M * N * K
+        for l in range(len(layers_w)):
+            for p, (_, K, N) in enumerate(synth.STACK_PROJS):
+                h = oracle.qlinear_w8a16(h, qi[l][p][0], qi[l][p][1], "int8")
+                flops += 2 * M * N * K
         h = x
-        for p, (_, K, N) in enumerate(synth.STACK_PROJS):
-            s = np.float32(sx[p])
-            xq = oracle.quantize_act_static(h, s, "fp8_e4m3fn")
-            h = oracle.qlinear_w8a8_static(xq, s, qf[p][0], qf[p][1], "fp8_e4m3fn")
-            flops += 2 * M * N * K
+        for l in range(len(layers_w)):
+            for p, (_, K, N) in enumerate(synth.STACK_PROJS):
+                s = np.float32(sx[l][p])
+                xq = oracle.quantize_act_static(h, s, "fp8_e4m3fn")
+                h = oracle.qlinear_w8a8_static(xq, s, qf[l][p][0], qf[l][p][1], "fp8_e4m3fn")
+                flops += 2 * M * N * K
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt, "cpu": platform.processor() or platform.machine(),
-            "sample": "layer 0 of the stack (q_proj, up_proj, down_proj chained), INT8 W8A16 and FP8 W8A8 "
+            "sample": f"layers 0-{len(layers_w) - 1} of the stack (q_proj, up_proj, down_proj chained), "
+                      "INT8 W8A16 and FP8 W8A8 "
                       "(activation quantization included, offline weight quantization and calibration "
                       "excluded), M in {1,16,256,1024}; float64 NumPy oracle"}
 
@@ -626,8 +633,8 @@ def main():
         log("[bench] copy calibration: 256 MiB read + 256 MiB written")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on its sample ...")
-        layer0 = [synth.stack_weight(args.seed, 0, p, dev) for p in range(3)]
-        line["cpu_baseline"] = cpu_baseline(args.seed, layer0, sx[0])
+        lw = [[synth.stack_weight(args.seed, l, p, dev) for p in range(3)] for l in range(CPU_SAMPLE_LAYERS)]
+        line["cpu_baseline"] = cpu_baseline(args.seed, lw, sx[:CPU_SAMPLE_LAYERS])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
