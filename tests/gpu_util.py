@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: moving seeded inputs to the device and the
-spec tolerance on bf16/fp32 results."""
+tolerance on bf16/fp32 results (relL2 <= 4e-3 and |err| <= 8e-3 (|ref| + rms(ref)))."""
 import numpy as np
 import torch
 
