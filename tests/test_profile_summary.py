@@ -69,3 +69,14 @@ def test_mfma_utilisation_and_traffic_calibration(tmp_path, capsys):
     out = capsys.readouterr().out
     assert "factors 2.000 (fetch), 1.000 (write)" in out
     assert f"fabric_bytes_per_launch: {2 * 1000 * 1024 + 500 * 1024}" in out
+
+
+def test_family_statistics(tmp_path, capsys):
+    rows = [{"Kernel_Name": K, "Start_Timestamp": 0, "End_Timestamp": 1000 * d, "Workgroup_Size_X": 512,
+             "Grid_Size_X": 512} for d in (10, 20, 30)]
+    rows.append({"Kernel_Name": "other", "Start_Timestamp": 0, "End_Timestamp": 999000, "Workgroup_Size_X": 64,
+                 "Grid_Size_X": 64})
+    p = tmp_path / "t.csv"
+    _write(p, TRACE_COLS, rows)
+    ps.family(str(p), r"gemm_mfma_kernel<0, 0")
+    assert "family_mean_us: 20.000" in capsys.readouterr().out

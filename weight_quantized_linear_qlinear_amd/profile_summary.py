@@ -1,11 +1,13 @@
 """Summaries of rocprofv3 CSV output for the library's kernels.
 
     python -m weight_quantized_linear_qlinear_amd.profile_summary kernels TRACE.csv [--top N]
+    python -m weight_quantized_linear_qlinear_amd.profile_summary family TRACE.csv REGEX
     python -m weight_quantized_linear_qlinear_amd.profile_summary mfma COUNTERS.csv AGENT_INFO.csv [--match RE]
     python -m weight_quantized_linear_qlinear_amd.profile_summary traffic FETCH.csv WRITE.csv [--match RE]
 
 `kernels` reads a `--kernel-trace` CSV and prints, per kernel and launch size
-(workgroups), the call count and the duration's mean, p10, p50, p90, min and max.
+(workgroups), the call count and the duration's mean, p10, p50, p90, min and max;
+`family` the same statistics over every dispatch whose kernel name matches REGEX.
 
 `mfma` reads a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE ...` CSV and prints per
 kernel and launch size the MFMA utilisation: the matrix-pipe busy cycles over all
@@ -57,6 +59,19 @@ def kernels(path: str, top: int):
         print(f"{name} | {wgs} x {wg} | {a.size} | {a.mean():.2f} | {np.percentile(a, 10):.2f} | "
               f"{np.percentile(a, 50):.2f} | {np.percentile(a, 90):.2f} | {a.min():.2f} | {a.max():.2f} | "
               f"{100 * a.sum() / total:.2f}")
+
+
+def family(path: str, match: str):
+    """Duration statistics over every dispatch whose kernel name matches `match`."""
+    rx = re.compile(match)
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(open(path))
+         if rx.search(r["Kernel_Name"])]
+    if not d:
+        raise SystemExit(f"no dispatch matches {match!r}")
+    a = np.array(d)
+    print(f"family {match!r}: {a.size} dispatches, mean {a.mean():.2f} us, p10 {np.percentile(a, 10):.2f}, "
+          f"p50 {np.percentile(a, 50):.2f}, p90 {np.percentile(a, 90):.2f}, min {a.min():.2f}, max {a.max():.2f}")
+    print(f"family_mean_us: {a.mean():.3f}")
 
 
 def _pivot(path: str, match: str | None):
@@ -149,6 +164,9 @@ def main(argv=None):
     k = sub.add_parser("kernels")
     k.add_argument("trace")
     k.add_argument("--top", type=int, default=40)
+    f = sub.add_parser("family")
+    f.add_argument("trace")
+    f.add_argument("match")
     m = sub.add_parser("mfma")
     m.add_argument("counters")
     m.add_argument("agent_info")
@@ -160,6 +178,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
         kernels(a.trace, a.top)
+    elif a.cmd == "family":
+        family(a.trace, a.match)
     elif a.cmd == "mfma":
         mfma(a.counters, a.agent_info, a.match)
     else:
