@@ -110,7 +110,7 @@ GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
   constexpr int64_t kCUs = 256;
   const int64_t KT = cdiv(K, 64);
   constexpr int kCfgs = 9;
-  // {W8A16, W8A8} x cfg 0..8 (cfgs 5, 6 and 8 are W8A8 only)
+  // {W8A16, W8A8} x cfg 0..8 (cfgs 5, 6 and 8 are W8A8 only; a zero t leaves a cfg out)
   const double t_us[2][kCfgs] = {{1.044, 0.7, 0.951, 0.716, 1.445, 0.0, 0.0, 0.617, 0.0},
                                  {0.639, 0.472, 0.571, 0.326, 0.919, 0.68, 0.601, 0.468, 0.324}};
   const double e_us[2][kCfgs] = {{6.105, 3.393, 6.54, 4.038, 13.98, 0.0, 0.0, 3.455, 0.0},
@@ -123,7 +123,7 @@ GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
   GemmPlan best;
   double best_cost = 1e300;
   for (int cfg = 0; cfg < kCfgs && cfg < mfma_num_cfgs(); ++cfg) {
-    if (!mfma_cfg_valid(scheme, cfg)) continue;
+    if (!mfma_cfg_valid(scheme, cfg) || !(t_us[sch][cfg] > 0.0)) continue;
     const int64_t BKT = mfma_cfg_bkt(cfg);
     if (KT % BKT != 0) continue;
     const int64_t KS = KT / BKT;                                // LDS stages over K

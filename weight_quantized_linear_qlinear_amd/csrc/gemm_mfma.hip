@@ -61,6 +61,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 0x3) << 14));
 }
 
+// The same with every LDS read of the wave returned (lgkmcnt 0) as well.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds_reads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (((N >> 4) & 0x3) << 14));
+}
+
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds, 16, 0, 0);
 }
@@ -246,10 +253,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 #pragma unroll
       for (int j = 0; j < TN; ++j) bc[h][j] = lds_read16(base + b_off(wn * TN + j, h >> 1, 2 * (h & 1) + kg));
   };
-  auto b_quarter = [&](const u32x4 (&bc)[2 * BKT][TN], int q, int j, int h) -> u32x2 {
-    const u32x4 c = bc[q >> 1][j];
-    const uint32_t d = (q & 1) ? (h ? c.w : c.z) : (h ? c.y : c.x);
-    return dequant4<QT>(d, sc[j], sc_m128[j]);
+  // Two codes of step q's B fragment of column block j (half h, pair e of its four
+  // codes) -> two bf16 of fp32(q) * s, as dequant4.  INT8 flips the sign bits of
+  // the word at pair 0 and keeps it for pair 1.
+  uint32_t xw[TN][2];
+  auto b_pair = [&](const u32x4 (&bc)[2 * BKT][TN], int q, int j, int h, int e) -> uint32_t {
+    const u32x4 cw = bc[q >> 1][j];
+    const uint32_t d = (q & 1) ? (h ? cw.w : cw.z) : (h ? cw.y : cw.x);
+    if constexpr (QT == kFp8) {
+      const f32x2 v = e ? __builtin_amdgcn_cvt_pk_f32_fp8((int)d, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)d, false);
+      return pack_bf16x2(v.x * sc[j], v.y * sc[j]);
+    } else {
+      if (e == 0) xw[j][h] = d ^ 0x80808080u;
+      const uint32_t x = xw[j][h] >> (16 * e);
+      return pack_bf16x2(__builtin_fmaf((float)(x & 0xFF), sc[j], sc_m128[j]),
+                         __builtin_fmaf((float)((x >> 8) & 0xFF), sc[j], sc_m128[j]));
+    }
   };
 
   // ---- pipeline: NSTAGE-1 stages in flight ahead of the one being consumed.
@@ -264,11 +283,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     // reads and dequantizes step 0 of the next stage, and it issues the DMAs
     // of stage t + NSTAGE into the slot of stage t, whose last reader passed
     // the barrier.  Each stage's DMAs get NSTAGE - 1 whole stages to land.
-    constexpr int Q = 4 * BKT, NM = TM * TN, DPM = (LOADS + NM - 1) / NM;
+    //
+    // With one row of waves (WAVES_M == 1) every wave copies exactly the weight
+    // tiles it reads (its own columns), so it may read the next stage's codes as
+    // soon as its own DMAs of that stage are complete, one step before the
+    // barrier, and dequantize the next stage's first step across all of the
+    // last step's MFMAs.  With a two-stage ring that wait would come a step
+    // sooner after the DMAs were issued, which measured slower, so two-stage
+    // tiles keep the codes read after the barrier.
+    constexpr int Q = 4 * BKT, NM = TM * TN, DPM = (LOADS + NM - 1) / NM, NP = 4 * TN;
+    constexpr bool OWN_B = WAVES_M == 1 && NSTAGE >= 3;
+    static_assert(!OWN_B || B_PER_WAVE == TN * 2 * BKT, "each wave copies the weight tiles of its own columns");
     static_assert(TM >= 2 && NM >= 3, "W8A16 pipeline shape: the last step schedules its work from MFMA 2 on");
-    u32x4 bc[2 * BKT][TN];
+    u32x4 bc[2 * BKT][TN], bcn[2 * BKT][TN];                  // codes of this stage and (OWN_B) the next
     u32x4 af[2][TM];
-    u32x2 bq[2][TN][2];
+    uint32_t bq[2][TN][2][2];   // [buffer][column block][half][pair]: bf16x2 of the B operand
 #pragma unroll
     for (int t = 0; t < NSTAGE; ++t) issue(t < nst ? t : nst - 1, t);
     wait_vmcnt<LOADS * (NSTAGE - 1)>();
@@ -277,10 +306,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[0][i] = a_step(smem, 0, i);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      bq[0][j][0] = b_quarter(bc, 0, j, 0);
-      bq[0][j][1] = b_quarter(bc, 0, j, 1);
-    }
+    for (int p = 0; p < NP; ++p) bq[0][p >> 2][(p >> 1) & 1][p & 1] = b_pair(bc, 0, p >> 2, (p >> 1) & 1, p & 1);
     for (int t = 0; t < nst; ++t) {
       const uint8_t* cur = smem + (t % NSTAGE) * STAGE;
       const uint8_t* nxt = smem + ((t + 1) % NSTAGE) * STAGE;   // past the end: a valid slot, unused
@@ -289,40 +315,54 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int c = q & 1;
+        if (OWN_B && q == Q - 2) wait_vmcnt<LOADS * (NSTAGE - 2)>();   // this wave's DMAs of stage t+1
         if (q == Q - 1) {
           // Stage t+1 visible, slot t free.  This wave's DMAs of stage t+1 are
-          // complete (vmcnt) and its reads of slot t were consumed, so no
-          // release fence: one would also wait for the younger stages' DMAs.
-          wait_vmcnt<LOADS * (NSTAGE - 2)>();
+          // complete (vmcnt) and its reads of slot t have returned (lgkmcnt),
+          // so no release fence: one would also wait for the younger stages' DMAs.
+          wait_vmcnt_lds_reads<LOADS * (NSTAGE - 2)>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           const int i = m / TN, j = m % TN;
-          const u32x4 bv = (u32x4){bq[c][j][0].x, bq[c][j][0].y, bq[c][j][1].x, bq[c][j][1].y};
+          const u32x4 bv = (u32x4){bq[c][j][0][0], bq[c][j][0][1], bq[c][j][1][0], bq[c][j][1][1]};
           accf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bv),
                                                                 __builtin_bit_cast(bf16x8, af[c][i]), accf[i][j], 0, 0, 0);
           if (q + 1 < Q) {
+            // step q+1's dequantization spread evenly over this step's MFMAs
 #pragma unroll
-            for (int pc = 0; pc < 2 * TN; ++pc)
-              if (m == pc * NM / (2 * TN)) bq[c ^ 1][pc >> 1][pc & 1] = b_quarter(bc, q + 1, pc >> 1, pc & 1);
+            for (int p = 0; p < NP; ++p)
+              if (m == p * NM / NP) bq[c ^ 1][p >> 2][(p >> 1) & 1][p & 1] = b_pair(bc, q + 1, p >> 2, (p >> 1) & 1, p & 1);
             if (m < TM) af[c ^ 1][m] = a_step(cur, q + 1, m);   // early in the step: ready by its end
+            if (OWN_B && q == Q - 2 && m == 0) read_codes(nxt, bcn);
           } else {
 #pragma unroll
             for (int d = 0; d < DPM; ++d)
               if (m * DPM + d < LOADS) dma_one(pf, t % NSTAGE, m * DPM + d);
-            if (m == 0) read_codes(nxt, bc);
-            if (m == 1) {
+            if (!OWN_B && m == 0) read_codes(nxt, bc);
+            if (m == (OWN_B ? 0 : 1)) {
 #pragma unroll
               for (int ii = 0; ii < TM; ++ii) af[c ^ 1][ii] = a_step(nxt, 0, ii);
             }
 #pragma unroll
-            for (int pc = 0; pc < 2 * TN; ++pc)
-              if (m == 2 + pc * (NM - 2) / (2 * TN)) bq[c ^ 1][pc >> 1][pc & 1] = b_quarter(bc, 0, pc >> 1, pc & 1);
+            for (int p = 0; p < NP; ++p) {
+              if constexpr (OWN_B) {
+                if (m == p * NM / NP) bq[c ^ 1][p >> 2][(p >> 1) & 1][p & 1] = b_pair(bcn, 0, p >> 2, (p >> 1) & 1, p & 1);
+              } else {
+                if (m == 2 + p * (NM - 2) / NP) bq[c ^ 1][p >> 2][(p >> 1) & 1][p & 1] = b_pair(bc, 0, p >> 2, (p >> 1) & 1, p & 1);
+              }
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      if constexpr (OWN_B) {
+#pragma unroll
+        for (int h = 0; h < 2 * BKT; ++h)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bc[h][j] = bcn[h][j];
       }
     }
   } else {
@@ -379,7 +419,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
         const uint8_t* src = q + 1 < Q ? cur : nxt;            // operands of the following step
         const int qn = q + 1 < Q ? q + 1 : 0;
         if (q == Q - 1) {                                      // as in the W8A16 loop
-          wait_vmcnt<LOADS * (NSTAGE - 2)>();
+          wait_vmcnt_lds_reads<LOADS * (NSTAGE - 2)>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         }
