@@ -331,6 +331,32 @@ def test_requant_parity_shapes_reach_every_plan_of_the_stack_chain():
                 assert k in tested, (qtype, M, name, k)
 
 
+def test_parity_shapes_reach_every_large_m_plan():
+    """Every large-M plan (tile configuration, split or not) the planner chooses over a
+    grid of shapes, for both schemes, is taken by a GPU parity shape (test_gpu_gemm.py's
+    small shapes or test_gpu_plans.py's), so no instantiation of the direct-to-LDS
+    kernel the library can launch goes without an oracle comparison."""
+    from tests.test_gpu_gemm import SHAPES
+    from tests.test_gpu_plans import W8A16_PLAN_SHAPES, W8A8_PLAN_SHAPES
+
+    def key(p):
+        return p["cfg"], p["split_k"] > 1
+
+    grid = [(M, K, N) for M in range(17, 1100, 48) for K in range(64, 11100, 64 * 7)
+            for N in range(100, 15000, 457)]
+    for scheme, extra in (("w8a16", W8A16_PLAN_SHAPES), ("w8a8_static", W8A8_PLAN_SHAPES)):
+        for qtype in ("int8", "fp8_e4m3fn"):
+            tested = set()
+            for mkn in list(SHAPES) + list(extra):
+                p = qlq.gemm_plan(scheme, *mkn, qtype)
+                if p["kind"] == 2:
+                    tested.add(key(p))
+            for mkn in grid:
+                p = qlq.gemm_plan(scheme, *mkn, qtype)
+                if p["kind"] == 2:
+                    assert key(p) in tested, (scheme, qtype, mkn, p)
+
+
 def test_noalloc_call_validates_on_the_host():
     """The allocation-free W8A16 call checks its arguments, and that its plan fits the
     library's scratch array, before it looks up a device (no GPU here)."""

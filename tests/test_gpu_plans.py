@@ -1,0 +1,73 @@
+"""Parity of every large-M launch plan (tile configuration, split or not) that the
+planner chooses, beyond the ones the small shapes of test_gpu_gemm.py reach.
+
+The direct-to-LDS kernel has one instantiation per tile configuration, and the
+loop of each differs (waves per tile, stages, whether a wave copies exactly the
+weight tiles it reads); the planner takes several of them only for large
+problems.  Each shape below is a small ragged (M, N) case that the planner sends
+to the plan named beside it; test_abi.py checks that these shapes together with
+test_gpu_gemm.py's reach every plan the planner chooses over a grid of shapes,
+so a refit of the planner cannot leave a plan without an oracle comparison.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import weight_quantized_linear_qlinear_amd as qlq
+from tests.gpu_util import bf16_bits, bf16_to_gpu, bits_to_f64, check_close, codes
+from tests.test_gpu_gemm import _prep
+
+pytestmark = pytest.mark.gpu
+
+QTYPES = ["int8", "fp8_e4m3fn"]
+# (M, K, N) -> (tile configuration, split-K) of the W8A16 planner
+W8A16_PLAN_SHAPES = [(257, 64, 11072),    # 128x256, four-stage ring, no split
+                     (17, 6976, 11072),   # 128x256, four-stage ring, K slices
+                     (257, 640, 11072),   # 128x256, two-stage ring, no split
+                     (17, 6400, 11072),   # 128x256, two-stage ring, K slices
+                     (769, 256, 14026),   # 256x256, no split
+                     (129, 5824, 11072)]  # 256x256, K slices
+# (M, K, N) of the W8A8 planner
+W8A8_PLAN_SHAPES = [(769, 1024, 14026),   # 256x256 eight waves, no split
+                    (385, 8320, 8329),    # 256x256 eight waves, K slices
+                    (513, 6976, 13393),   # 256x256 three-stage ring, no split
+                    (535, 512, 13175),    # 256x192, no split
+                    (129, 9472, 11072),   # 256x192, K slices
+                    (17, 1216, 100)]      # 128x128 four waves, K slices
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("MKN", W8A16_PLAN_SHAPES)
+def test_w8a16_plan_parity(qtype, MKN):
+    M, K, N = MKN
+    plan = qlq.gemm_plan("w8a16", M, K, N, qtype)
+    print(f"w8a16 {qtype} M={M} K={K} N={N} plan {plan}", flush=True)
+    assert plan["kind"] == 2
+    _, _, x, qw, q_ref, s_ref = _prep(4000 + M * 7 + K + N, M, K, N, qtype)
+    y = qlq.qlinear_w8a16(bf16_to_gpu(x), qw)
+    ref = oracle.qlinear_w8a16(x, q_ref, s_ref, qtype)
+    check_close(bits_to_f64(bf16_bits(y)), bits_to_f64(ref), f"w8a16 {qtype} {MKN}")
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("MKN", W8A8_PLAN_SHAPES)
+def test_w8a8_plan_parity(qtype, MKN):
+    M, K, N = MKN
+    plan = qlq.gemm_plan("w8a8_static", M, K, N, qtype)
+    print(f"w8a8 {qtype} M={M} K={K} N={N} plan {plan}", flush=True)
+    assert plan["kind"] == 2
+    _, calib, x, qw, q_ref, s_ref = _prep(5000 + M * 7 + K + N, M, K, N, qtype)
+    sx = oracle.calibrate_input_scale(calib, qtype)
+    xq_ref = oracle.quantize_act_static(x, sx, qtype)
+    xq = qlq.quantize_act_static(bf16_to_gpu(x), float(sx), qtype)
+    assert np.array_equal(codes(xq), xq_ref.view(np.uint8))
+    acc = qlq.qlinear_w8a8_static(xq, float(sx), qw, "acc").cpu().numpy()
+    acc_ref = oracle.qlinear_w8a8_static(xq_ref, sx, q_ref, s_ref, qtype, out="acc")
+    y = bf16_bits(qlq.qlinear_w8a8_static(xq, float(sx), qw, "bf16"))
+    y_ref = oracle.qlinear_w8a8_static(xq_ref, sx, q_ref, s_ref, qtype)
+    if qtype == "int8":                                   # exact int32 accumulators
+        assert np.array_equal(acc, acc_ref)
+        assert np.array_equal(y, y_ref)
+    else:
+        check_close(acc, acc_ref, f"fp8 acc {MKN}")
+        check_close(bits_to_f64(y), bits_to_f64(y_ref), f"fp8 y {MKN}")
