@@ -331,30 +331,34 @@ def test_requant_parity_shapes_reach_every_plan_of_the_stack_chain():
                 assert k in tested, (qtype, M, name, k)
 
 
-def test_parity_shapes_reach_every_large_m_plan():
-    """Every large-M plan (tile configuration, split or not) the planner chooses over a
-    grid of shapes, for both schemes, is taken by a GPU parity shape (test_gpu_gemm.py's
-    small shapes or test_gpu_plans.py's), so no instantiation of the direct-to-LDS
-    kernel the library can launch goes without an oracle comparison."""
-    from tests.test_gpu_gemm import SHAPES
-    from tests.test_gpu_plans import W8A16_PLAN_SHAPES, W8A8_PLAN_SHAPES
+def test_parity_shapes_reach_every_launch_plan():
+    """Every launch plan the planner chooses over a grid of shapes, for both schemes and
+    qtypes, is taken by a GPU parity shape (test_gpu_gemm.py's or test_gpu_plans.py's),
+    so no kernel instantiation the library can launch goes without an oracle comparison.
+    A plan is, for large M, the kernel (direct-to-LDS for K a multiple of 64, else
+    register-staged), its tile configuration and whether K is split; for small M, the
+    waves per workgroup, whether K is split and whether K is a multiple of 64 (the aligned
+    path)."""
+    from tests.test_gpu_gemm import PAIR_SHAPES, SHAPES
+    from tests.test_gpu_plans import SMALL_PLAN_SHAPES, W8A16_PLAN_SHAPES, W8A8_PLAN_SHAPES
 
-    def key(p):
-        return p["cfg"], p["split_k"] > 1
+    def key(mkn, p):
+        if p["kind"] == 0:
+            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0
+        return p["kind"], p["cfg"], p["split_k"] > 1
 
     grid = [(M, K, N) for M in range(17, 1100, 48) for K in range(64, 11100, 64 * 7)
             for N in range(100, 15000, 457)]
+    grid += [(M, K, N) for M in (17, 300, 1000) for K in (100, 1000, 1727, 5000) for N in (100, 2000, 11000)]
+    grid += [(M, K, N) for M in (1, 2, 5, 16) for K in list(range(64, 16400, 320)) + [100, 1000, 1727]
+             for N in range(16, 15000, 397)]
     for scheme, extra in (("w8a16", W8A16_PLAN_SHAPES), ("w8a8_static", W8A8_PLAN_SHAPES)):
         for qtype in ("int8", "fp8_e4m3fn"):
-            tested = set()
-            for mkn in list(SHAPES) + list(extra):
-                p = qlq.gemm_plan(scheme, *mkn, qtype)
-                if p["kind"] == 2:
-                    tested.add(key(p))
+            tested = {key(mkn, qlq.gemm_plan(scheme, *mkn, qtype))
+                      for mkn in list(SHAPES) + list(PAIR_SHAPES) + list(extra) + list(SMALL_PLAN_SHAPES)}
             for mkn in grid:
                 p = qlq.gemm_plan(scheme, *mkn, qtype)
-                if p["kind"] == 2:
-                    assert key(p) in tested, (scheme, qtype, mkn, p)
+                assert key(mkn, p) in tested, (scheme, qtype, mkn, p)
 
 
 def test_noalloc_call_validates_on_the_host():

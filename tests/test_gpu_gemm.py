@@ -19,13 +19,15 @@ QTYPES = ["int8", "fp8_e4m3fn"]
 # plans include 4, 8 and 16 waves per workgroup (e.g. (4, 4096, 8192): 8 waves, no split;
 # (1, 16384, 1024): 16 waves, two K slices; (2, 2048, 11008): 4 waves), and the aligned path's
 # every count of 1 to 8 K units per wave, for one and two 64-input tiles per unit (the K = 64 * odd
-# case (1, 1728, 2060) leaves the last FP8 W8A8 unit half past the end of K).
+# case (1, 1728, 2060) leaves the last FP8 W8A8 unit half past the end of K); M > 16 with K not a
+# multiple of 64 takes the register-staged kernel, with K slices (37, 1000, 300) and without
+# (300, 100, 1100).
 SHAPES = [(1, 1, 1), (1, 64, 16), (2, 5, 3), (8, 8, 8), (1, 2048, 2048), (3, 100, 37), (16, 640, 200),
           (13, 1000, 300), (16, 11008, 128), (17, 640, 200), (31, 512, 129), (33, 256, 64), (64, 128, 4096),
           (255, 1024, 136), (257, 320, 250), (130, 4096, 96), (128, 64, 128), (4, 4096, 8192), (5, 4096, 1024),
           (2, 2048, 11008), (512, 512, 1024), (3, 1792, 2060), (7, 1408, 2060), (9, 1280, 2060),
           (2, 3584, 2060), (11, 2816, 2060), (6, 2560, 2060), (1, 1728, 2060), (1, 16384, 1024),
-          (5, 1152, 2060)]
+          (5, 1152, 2060), (37, 1000, 300), (300, 100, 1100)]
 
 
 def _prep(seed, M, K, N, qtype, gran="per_channel"):

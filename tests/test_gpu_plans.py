@@ -1,5 +1,6 @@
-"""Parity of every large-M launch plan (tile configuration, split or not) that the
-planner chooses, beyond the ones the small shapes of test_gpu_gemm.py reach.
+"""Parity of every launch plan the planner chooses (large M: tile configuration, split or
+not; small M: waves per workgroup, split or not, aligned K or not), beyond the ones the
+small shapes of test_gpu_gemm.py reach.
 
 The direct-to-LDS kernel has one instantiation per tile configuration, and the
 loop of each differs (waves per tile, stages, whether a wave copies exactly the
@@ -36,13 +37,22 @@ W8A8_PLAN_SHAPES = [(769, 1024, 14026),   # 256x256 eight waves, no split
                     (17, 1216, 100)]      # 128x128 four waves, K slices
 
 
+# (M, K, N) -> small-M plans (waves per workgroup, K slices, aligned K or not) that the
+# small shapes of test_gpu_gemm.py leave out, for both schemes
+SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
+                     (7, 100, 1207),     # eight waves, no split, ragged K
+                     (11, 100, 2398),    # four waves, no split, ragged K
+                     (13, 1727, 413),    # eight waves, K slices, ragged K
+                     (16, 1000, 1207)]   # four waves, K slices, ragged K
+
+
 @pytest.mark.parametrize("qtype", QTYPES)
-@pytest.mark.parametrize("MKN", W8A16_PLAN_SHAPES)
+@pytest.mark.parametrize("MKN", W8A16_PLAN_SHAPES + SMALL_PLAN_SHAPES)
 def test_w8a16_plan_parity(qtype, MKN):
     M, K, N = MKN
     plan = qlq.gemm_plan("w8a16", M, K, N, qtype)
     print(f"w8a16 {qtype} M={M} K={K} N={N} plan {plan}", flush=True)
-    assert plan["kind"] == 2
+    assert plan["kind"] == (2 if M > 16 else 0)
     _, _, x, qw, q_ref, s_ref = _prep(4000 + M * 7 + K + N, M, K, N, qtype)
     y = qlq.qlinear_w8a16(bf16_to_gpu(x), qw)
     ref = oracle.qlinear_w8a16(x, q_ref, s_ref, qtype)
@@ -50,12 +60,12 @@ def test_w8a16_plan_parity(qtype, MKN):
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
-@pytest.mark.parametrize("MKN", W8A8_PLAN_SHAPES)
+@pytest.mark.parametrize("MKN", W8A8_PLAN_SHAPES + SMALL_PLAN_SHAPES)
 def test_w8a8_plan_parity(qtype, MKN):
     M, K, N = MKN
     plan = qlq.gemm_plan("w8a8_static", M, K, N, qtype)
     print(f"w8a8 {qtype} M={M} K={K} N={N} plan {plan}", flush=True)
-    assert plan["kind"] == 2
+    assert plan["kind"] == (2 if M > 16 else 0)
     _, calib, x, qw, q_ref, s_ref = _prep(5000 + M * 7 + K + N, M, K, N, qtype)
     sx = oracle.calibrate_input_scale(calib, qtype)
     xq_ref = oracle.quantize_act_static(x, sx, qtype)
