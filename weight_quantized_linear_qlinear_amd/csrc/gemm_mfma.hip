@@ -29,8 +29,8 @@
 //    banks; otherwise A fragments land in MFMA lane order.  B is the packed
 //    weight tile copied verbatim (8 whole lines per instruction) and read with
 //    per-lane addresses;
-//  * W8A16 dequantizes B in registers after the LDS read, four codes at a
-//    time: bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
+//  * W8A16 dequantizes B in registers after the LDS read, two codes after
+//    each MFMA: bf16(fp32(q) * s[n]), the rounding the weight-only scheme prescribes;
 //  * per-wave tiles of 128 rows (or 64 with 8 waves) keep LDS traffic within
 //    budget; W8A16 tiles give each wave its own weight columns where they can,
 //    so a column is dequantized once per workgroup (128x128 as 1 x 4 waves).
@@ -254,7 +254,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
       for (int j = 0; j < TN; ++j) bc[h][j] = lds_read16(base + b_off(wn * TN + j, h >> 1, 2 * (h & 1) + kg));
   };
   // Two codes of step q's B fragment of column block j (half h, pair e of its four
-  // codes) -> two bf16 of fp32(q) * s, as dequant4.  INT8 flips the sign bits of
+  // codes) -> two bf16 of fp32(q) * s, rounded as in dequant8.  INT8 flips the sign bits of
   // the word at pair 0 and keeps it for pair 1.
   uint32_t xw[TN][2];
   auto b_pair = [&](const u32x4 (&bc)[2 * BKT][TN], int q, int j, int h, int e) -> uint32_t {

@@ -188,20 +188,6 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t d0, uint32_t d1, float s, fl
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Four codes (one 32-bit word) -> four bf16 of fp32(q) * s, as dequant8 above.
-template <int QT>
-__device__ __forceinline__ u32x2 dequant4(uint32_t d, float s, float s_m128) {
-  if constexpr (QT == kFp8) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, true);
-    return (u32x2){pack_bf16x2(lo.x * s, lo.y * s), pack_bf16x2(hi.x * s, hi.y * s)};
-  } else {
-    const uint32_t e = d ^ 0x80808080u;
-    return (u32x2){pack_bf16x2(__builtin_fmaf((float)(e & 0xFF), s, s_m128), __builtin_fmaf((float)((e >> 8) & 0xFF), s, s_m128)),
-                   pack_bf16x2(__builtin_fmaf((float)((e >> 16) & 0xFF), s, s_m128), __builtin_fmaf((float)(e >> 24), s, s_m128))};
-  }
-}
-
 // ---------------------------------------------------------------- MFMA wrappers
 // 16x16 output tiles; lane l holds D[4*(l/16) + j][l % 16], j = 0..3.
 // A operand: row l % 16, B operand: column l % 16; both carry the same k slots,
