@@ -18,7 +18,11 @@
 // thread owns 8 consecutive elements of a row (one 16-byte load of K and of V,
 // one 8-byte store of each's codes), so a wave streams 1 KiB of K and of V per
 // instruction; a K group is 4 neighbouring lanes and a row D / 8 lanes, both
-// reduced with xor-shuffles.  Any other head_dim takes a wave per (t, h) row
+// reduced with xor-shuffles.  Its loads and stores are non-temporal: each input
+// is read once and the codes go to the cache for later steps (measured on the 7B
+// shape, 28 layers: 8.4 -> 6.7 us per layer at 8192 tokens, 23.1 -> 21.9 at
+// 32768).  The dequantizer keeps ordinary stores: its output is read right away
+// by attention, and a scratch output reused layer after layer stays in the cache.  Any other head_dim takes a wave per (t, h) row
 // (lane l owns elements l + 64 j; a K group is a half-wave for one j).
 // Dequantizer: 8 elements per thread (one 8-byte code load, one 16-byte store),
 // the 8 sharing one K group and one V scale.  All are HBM-bound streams.
@@ -107,8 +111,8 @@ __global__ __launch_bounds__(256) void kv_quantize8_kernel(const uint16_t* __res
   for (int64_t it = 0; it < iters; ++it) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x + it * stride;
     const bool live = i < n8;
-    const u32x4 kc = live ? ld16(k + i * 8) : (u32x4){0u, 0u, 0u, 0u};
-    const u32x4 vc = live ? ld16(v + i * 8) : (u32x4){0u, 0u, 0u, 0u};
+    const u32x4 kc = live ? ld16_stream(k + i * 8) : (u32x4){0u, 0u, 0u, 0u};
+    const u32x4 vc = live ? ld16_stream(v + i * 8) : (u32x4){0u, 0u, 0u, 0u};
     const uint32_t kd[4] = {kc.x, kc.y, kc.z, kc.w}, vd[4] = {vc.x, vc.y, vc.z, vc.w};
     float ka = 0.0f, va = 0.0f;
 #pragma unroll
@@ -134,8 +138,8 @@ __global__ __launch_bounds__(256) void kv_quantize8_kernel(const uint16_t* __res
       vw[h] = f32x4_to_e4m3x4_sat(dv(bf16_bits_to_f32(c & 0xFFFF)), dv(bf16_bits_to_f32(c >> 16)),
                                   dv(bf16_bits_to_f32(d & 0xFFFF)), dv(bf16_bits_to_f32(d >> 16)));
     }
-    *reinterpret_cast<u32x2*>(kq + i * 8) = (u32x2){kw[0], kw[1]};
-    *reinterpret_cast<u32x2*>(vq + i * 8) = (u32x2){vw[0], vw[1]};
+    __builtin_nontemporal_store((u32x2){kw[0], kw[1]}, reinterpret_cast<u32x2*>(kq + i * 8));
+    __builtin_nontemporal_store((u32x2){vw[0], vw[1]}, reinterpret_cast<u32x2*>(vq + i * 8));
     if ((lane & 3) == 0) ks[i / 4] = (uint16_t)kb;            // chunk i starts group i / 4
     if ((lane & (TPR - 1)) == 0) vs[i / TPR] = (uint16_t)vb;  // chunk i starts row i / TPR
   }
