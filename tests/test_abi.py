@@ -313,7 +313,8 @@ def test_plan_hook_reports_the_kernel_families():
 
 
 def test_requant_parity_shapes_reach_every_plan_of_the_stack_chain():
-    """Every launch plan (kernel family, tile configuration, split or not, waves) that
+    """Every launch plan (kernel family, tile configuration, split or not, waves, tile
+    width) that
     the 3B-scale stack's W8A8 chain takes is also taken by a requantizing-epilogue
     parity shape, so a planner refit cannot leave a timed plan without an oracle
     comparison of its code-writing epilogue."""
@@ -321,7 +322,7 @@ def test_requant_parity_shapes_reach_every_plan_of_the_stack_chain():
     from tests.test_gpu_requant import SHAPES
 
     def key(p):
-        return p["kind"], p["cfg"], p["split_k"] > 1, p["waves"]
+        return p["kind"], p["cfg"], p["split_k"] > 1, p["waves"], p["tile_n"]
 
     for qtype in ("int8", "fp8_e4m3fn"):
         tested = {key(qlq.gemm_plan("w8a8_static", *mkn, qtype)) for mkn in SHAPES}
@@ -337,14 +338,14 @@ def test_parity_shapes_reach_every_launch_plan():
     so no kernel instantiation the library can launch goes without an oracle comparison.
     A plan is, for large M, the kernel (direct-to-LDS for K a multiple of 64, else
     register-staged), its tile configuration and whether K is split; for small M, the
-    waves per workgroup, whether K is split and whether K is a multiple of 64 (the aligned
-    path)."""
+    waves per workgroup, the 16-column tiles per workgroup, whether K is split and
+    whether K is a multiple of 64 (the aligned path)."""
     from tests.test_gpu_gemm import PAIR_SHAPES, SHAPES
     from tests.test_gpu_plans import SMALL_PLAN_SHAPES, W8A16_PLAN_SHAPES, W8A8_PLAN_SHAPES
 
     def key(mkn, p):
         if p["kind"] == 0:
-            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0
+            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0, p["tile_n"]
         return p["kind"], p["cfg"], p["split_k"] > 1
 
     grid = [(M, K, N) for M in range(17, 1100, 48) for K in range(64, 11100, 64 * 7)

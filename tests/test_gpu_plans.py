@@ -1,6 +1,6 @@
 """Parity of every launch plan the planner chooses (large M: tile configuration, split or
-not; small M: waves per workgroup, split or not, aligned K or not), beyond the ones the
-small shapes of test_gpu_gemm.py reach.
+not; small M: waves per workgroup, 16-column tiles per workgroup, split or not, aligned
+K or not), beyond the ones the small shapes of test_gpu_gemm.py reach.
 
 The direct-to-LDS kernel has one instantiation per tile configuration, and the
 loop of each differs (waves per tile, stages, whether a wave copies exactly the
@@ -37,13 +37,20 @@ W8A8_PLAN_SHAPES = [(769, 1024, 14026),   # 256x256 eight waves, no split
                     (17, 1216, 100)]      # 128x128 four waves, K slices
 
 
-# (M, K, N) -> small-M plans (waves per workgroup, K slices, aligned K or not) that the
-# small shapes of test_gpu_gemm.py leave out, for both schemes
+# (M, K, N) -> small-M plans (waves per workgroup, column tiles per workgroup, K slices,
+# aligned K or not) that the small shapes of test_gpu_gemm.py leave out, for both schemes
 SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (7, 100, 1207),     # eight waves, no split, ragged K
                      (11, 100, 2398),    # four waves, no split, ragged K
                      (13, 1727, 413),    # eight waves, K slices, ragged K
-                     (16, 1000, 1207)]   # four waves, K slices, ragged K
+                     (16, 1000, 1207),   # four waves, K slices, ragged K
+                     # several 16-column tiles per workgroup (the last group holds fewer);
+                     # tiles x waves for W8A16 / INT8 W8A8 / FP8 W8A8
+                     (13, 64, 10338),    # 4 x 4 / 2 x 4 / 4 x 4
+                     (14, 704, 10338),   # 4 x 8 / 2 x 8 / 4 x 4
+                     (12, 1024, 10338),  # 4 x 16 / 2 x 8 / 4 x 8
+                     (13, 1984, 5177),   # 2 x 16 / 2 x 16 / 2 x 8
+                     (13, 1984, 10338)]  # 4 x 16 / 2 x 16 / 4 x 16
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

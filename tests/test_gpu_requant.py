@@ -31,8 +31,9 @@ SHAPES = [(1, 1, 1), (1, 2048, 1024), (1, 2048, 2048), (3, 100, 37), (16, 640, 2
           (64, 128, 4096), (130, 4096, 96), (255, 1024, 136), (257, 320, 250), (256, 11008, 256),
           (1024, 2048, 1024), (130, 1000, 96), (40, 200, 64), (300, 2000, 300),
           # plans of the 3B-scale stack's chain: small-M without split (4 waves) and with split
-          # (8 / 16 waves), and the 256x192 tile the up projection takes at M = 1024
-          (1, 2048, 11008), (16, 11008, 2048), (768, 512, 11008)]
+          # (8 / 16 waves), two 16-column tiles per workgroup (up projection at M = 16), and
+          # the 256x192 tile the up projection takes at M = 1024
+          (1, 2048, 11008), (16, 11008, 2048), (16, 2048, 11008), (768, 512, 11008)]
 
 
 def _e4m3_step(v: np.ndarray) -> np.ndarray:

@@ -13,8 +13,9 @@
 // The W8A8 epilogue takes a per-token scale per row when the call passes one.
 // M <= 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
 //
-// Work split: workgroup (nt, s) owns output columns [16 nt, 16 nt + 16) and the
-// s-th slice of K; its NW (4, 8 or 16) waves take consecutive sub-slices.  The
+// Work split: workgroup (nt, s) owns output columns [16 nt, 16 nt + 16 CT) (CT
+// column tiles, see the kernel) and the s-th slice of K; its NW (4, 8 or 16) waves
+// take consecutive sub-slices.  The
 // wave accumulators are summed through LDS; with S > 1 slices per column block the
 // partial sums go to the workspace and the last workgroup to arrive adds them
 // in slice order (deterministic) and runs the epilogue.  The handoff uses
@@ -73,14 +74,34 @@ __device__ __forceinline__ u32x4 load_x_codes16(const uint8_t* row, int k, int K
   }
 }
 
-template <int QT, int SCH, bool FAST, int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, int ups, int upw) {
+// CT: 16-column tiles per workgroup (1, 2 or 4; more than one on the aligned path
+// without K slices).  A wave's x fragments of a unit then serve all CT column tiles
+// (each unit's CT weight loads are issued with its x loads), so every KiB of
+// weights brings 1/CT as many x bytes through the vector memory path; at M = 16 in
+// bf16 that is 2 KiB of x per KiB of weights with one tile.  A load batch holds
+// 8 / CT units, so the registers in flight stay those of eight single-tile units.
+// Four waves per SIMD (at most 128 registers per lane) let two 8-wave or four 4-wave
+// workgroups share a CU (16 waves hold a CU alone); FP8 W8A8 with one tile keeps the
+// registers its longer units take and runs three.
+template <int QT, int SCH, bool FAST, int NW, int CT = 1>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
+    (NW == 16 || (SCH == kW8A8 && QT == kFp8 && CT == 1)) ? 1 : 4))) void gemm_small_kernel(GemmArgs a, int S, int ups,
+                                                                                          int upw) {
   using T = SmallTraits<QT, SCH>;
   constexpr int TPU = T::kTilesPerUnit;
-  constexpr int kU = kUnroll;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nt = blockIdx.x % a.NT;
-  const int s = blockIdx.x / a.NT;
+  constexpr int kU = kUnroll / CT;                         // units per load batch
+  static_assert(CT == 1 || ((CT == 2 || CT == 4) && FAST), "several column tiles on the aligned path only");
+  // The wave index is uniform across the wave: reading it once keeps the unit range and
+  // the loop control in scalar registers.  Chosen per build: it pays with one tile
+  // except for 16-wave INT8 W8A16 (K-sliced down projections ran 3 % slower; the FP8
+  // build spills without it), and with several tiles the register allocation spills
+  // with it.
+  constexpr bool kScalarWave = CT == 1 && (NW < 16 || SCH == kW8A8 || QT == kFp8);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = kScalarWave ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  const int NTG = (a.NT + CT - 1) / CT;                       // column-tile groups
+  const int nt = (blockIdx.x % NTG) * CT;                     // first column tile of the group
+  const int s = blockIdx.x / NTG;
   const int KU = (a.KT + TPU - 1) / TPU;
   const int u_begin = s * ups + wave * upw;
   int u_end = u_begin + upw;
@@ -88,29 +109,38 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
   if (u_end > KU) u_end = KU;
 
   const int r = lane & 15, g = lane >> 4;
-  const int n = nt * kTileN + r;
-  float sc = 0.0f;
-  if (SCH == kW8A16) sc = a.scale_per_tensor ? a.w_scale[0] : (n < a.N ? a.w_scale[n] : 0.0f);
-  const float sc_m128 = -128.0f * sc;
+  float sc[CT], sc_m128[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int nc = (nt + c) * kTileN + r;
+    sc[c] = 0.0f;
+    if (SCH == kW8A16) sc[c] = a.scale_per_tensor ? a.w_scale[0] : (nc < a.N ? a.w_scale[nc] : 0.0f);
+    sc_m128[c] = -128.0f * sc[c];
+  }
 
   // Row m = r of the A operand; rows >= M contribute zeros.
   const bool row_ok = r < a.M;
   const uint8_t* wbase = a.w + (int64_t)nt * a.KT * kTileBytes + lane * 16;
 
-  f32x4 accf = {0.f, 0.f, 0.f, 0.f};
-  i32x4 acci = {0, 0, 0, 0};
+  f32x4 accf[CT];
+  i32x4 acci[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    accf[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acci[c] = (i32x4){0, 0, 0, 0};
+  }
 
-  // A unit's arithmetic: dequantize (W8A16) and feed the MFMA.
-  auto unit_mma = [&](const u32x4 (&wv)[TPU], const u32x4 (&xa)[TPU], const u32x4 (&xb)[TPU]) {
+  // A unit's arithmetic for column tile c: dequantize (W8A16) and feed the MFMA.
+  auto unit_mma = [&](int c, const u32x4 (&wv)[TPU], const u32x4 (&xa)[TPU], const u32x4 (&xb)[TPU]) {
     if constexpr (SCH == kW8A16) {
-      bf16x8 b0 = dequant8<QT>(wv[0].x, wv[0].y, sc, sc_m128);
-      bf16x8 b1 = dequant8<QT>(wv[0].z, wv[0].w, sc, sc_m128);
-      accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[0]), b0, accf);
-      accf = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[0]), b1, accf);
+      bf16x8 b0 = dequant8<QT>(wv[0].x, wv[0].y, sc[c], sc_m128[c]);
+      bf16x8 b1 = dequant8<QT>(wv[0].z, wv[0].w, sc[c], sc_m128[c]);
+      accf[c] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[0]), b0, accf[c]);
+      accf[c] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[0]), b1, accf[c]);
     } else if constexpr (QT == kInt8) {
-      acci = mfma_i8_k64(xa[0], wv[0], acci);
+      acci[c] = mfma_i8_k64(xa[0], wv[0], acci[c]);
     } else {
-      accf = mfma_fp8_k128(xa[0], xa[TPU - 1], wv[0], wv[TPU - 1], accf);
+      accf[c] = mfma_fp8_k128(xa[0], xa[TPU - 1], wv[0], wv[TPU - 1], accf[c]);
     }
   };
 
@@ -124,22 +154,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
     // unit); zero codes and zero activations add +0 to an accumulator that starts
     // at +0, so the sums are unchanged.  Offsets stay below 2^31: M <= 16 and
     // K <= 2^24 bound both buffers to 2^29 bytes.
+    // The group's column tiles are consecutive in the packed weights; a tile past the
+    // last one lies past the range and reads zeros.  With several column tiles the K
+    // tile past the end of tile c would be the first K tile of tile c + 1, so that tile's
+    // weight and x offsets are moved past both ranges instead.
+    const int tiles_here = a.NT - nt < CT ? a.NT - nt : CT;
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.w) + (int64_t)nt * a.KT * kTileBytes, 0, a.KT * kTileBytes, kBufferWord3);
+        const_cast<uint8_t*>(a.w) + (int64_t)nt * a.KT * kTileBytes, 0, tiles_here * a.KT * kTileBytes,
+        kBufferWord3);
     constexpr int kEsz = SCH == kW8A16 ? 2 : 1;
     const __amdgpu_buffer_rsrc_t xrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), 0, a.M * a.K * kEsz, kBufferWord3);
     const uint32_t xrow = row_ok ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
     auto run = [&](int u0, auto nu) {
       constexpr int NU = decltype(nu)::value;
-      u32x4 wv[NU][TPU], xa[NU][TPU], xb[NU][TPU];
+      u32x4 wv[NU][CT][TPU], xa[NU][TPU], xb[NU][TPU];
 #pragma unroll
       for (int i = 0; i < NU; ++i) {
 #pragma unroll
         for (int t = 0; t < TPU; ++t) {
           const int kt = (u0 + i) * TPU + t;
-          const uint32_t xo = xrow + (uint32_t)(kt * kTileK * kEsz);
-          wv[i][t] = __builtin_amdgcn_raw_buffer_load_b128(wrs, kt * kTileBytes + lane * 16, 0, kCachePolicyNt);
+          const bool kt_in = TPU == 1 || CT == 1 || kt < a.KT;
+          const uint32_t xo = kt_in ? xrow + (uint32_t)(kt * kTileK * kEsz) : 0x80000000u;
+#pragma unroll
+          for (int c = 0; c < CT; ++c)
+            wv[i][c][t] = __builtin_amdgcn_raw_buffer_load_b128(
+                wrs, kt_in ? (c * a.KT + kt) * kTileBytes + lane * 16 : (int)0x80000000u, 0, kCachePolicyNt);
           xa[i][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0);
           xb[i][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(xo + 16), 0, 0)
                                    : (u32x4){0u, 0u, 0u, 0u};
@@ -148,20 +188,34 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
       }
 #pragma unroll
       for (int i = 0; i < NU; ++i) {
-        unit_mma(wv[i], xa[i], xb[i]);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) unit_mma(c, wv[i][c], xa[i], xb[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     for (int u0 = u_begin; u0 < u_end; u0 += kU) {
-      switch (u_end - u0 < kU ? u_end - u0 : kU) {
-        case 1: run(u0, std::integral_constant<int, 1>{}); break;
-        case 2: run(u0, std::integral_constant<int, 2>{}); break;
-        case 3: run(u0, std::integral_constant<int, 3>{}); break;
-        case 4: run(u0, std::integral_constant<int, 4>{}); break;
-        case 5: run(u0, std::integral_constant<int, 5>{}); break;
-        case 6: run(u0, std::integral_constant<int, 6>{}); break;
-        case 7: run(u0, std::integral_constant<int, 7>{}); break;
-        default: run(u0, std::integral_constant<int, 8>{}); break;
+      const int nb = u_end - u0 < kU ? u_end - u0 : kU;
+      if constexpr (kU == 2) {
+        if (nb == 1) run(u0, std::integral_constant<int, 1>{});
+        else run(u0, std::integral_constant<int, 2>{});
+      } else if constexpr (kU == 8) {
+        switch (nb) {
+          case 1: run(u0, std::integral_constant<int, 1>{}); break;
+          case 2: run(u0, std::integral_constant<int, 2>{}); break;
+          case 3: run(u0, std::integral_constant<int, 3>{}); break;
+          case 4: run(u0, std::integral_constant<int, 4>{}); break;
+          case 5: run(u0, std::integral_constant<int, 5>{}); break;
+          case 6: run(u0, std::integral_constant<int, 6>{}); break;
+          case 7: run(u0, std::integral_constant<int, 7>{}); break;
+          default: run(u0, std::integral_constant<int, 8>{}); break;
+        }
+      } else {
+        switch (nb) {
+          case 1: run(u0, std::integral_constant<int, 1>{}); break;
+          case 2: run(u0, std::integral_constant<int, 2>{}); break;
+          case 3: run(u0, std::integral_constant<int, 3>{}); break;
+          default: run(u0, std::integral_constant<int, 4>{}); break;
+        }
       }
     }
   } else {
@@ -194,29 +248,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
 #pragma unroll
       for (int i = 0; i < kU; ++i) {
         if (u0 + i >= u_end) break;
-        unit_mma(wv[i], xa[i], xb[i]);
+        unit_mma(0, wv[i], xa[i], xb[i]);
       }
     }
   }
 
-  // ---- sum the waves through LDS (wave 0 finishes the job)
-  __shared__ f32x4 red[NW][64];
-  f32x4 mine = T::kIntAcc ? __builtin_bit_cast(f32x4, acci) : accf;
-  red[wave][lane] = mine;
+  // ---- sum the waves through LDS (wave c finishes column tile nt + c)
+  __shared__ f32x4 red[CT][NW][64];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) red[c][wave][lane] = T::kIntAcc ? __builtin_bit_cast(f32x4, acci[c]) : accf[c];
   __syncthreads();
-  if (wave != 0) return;
+  if (wave >= CT || nt + wave >= a.NT) return;
+  const int cw = CT == 1 ? 0 : wave;
   f32x4 tot;
   if constexpr (T::kIntAcc) {
-    i32x4 t = __builtin_bit_cast(i32x4, red[0][lane]);
-    for (int w = 1; w < NW; ++w) t += __builtin_bit_cast(i32x4, red[w][lane]);
+    i32x4 t = __builtin_bit_cast(i32x4, red[cw][0][lane]);
+    for (int w = 1; w < NW; ++w) t += __builtin_bit_cast(i32x4, red[cw][w][lane]);
     tot = __builtin_bit_cast(f32x4, t);
   } else {
-    tot = red[0][lane];
-    for (int w = 1; w < NW; ++w) tot += red[w][lane];
+    tot = red[cw][0][lane];
+    for (int w = 1; w < NW; ++w) tot += red[cw][w][lane];
   }
 
-  // ---- split-K: publish, count arrivals, last one sums the slices in order
-  if (S > 1) {
+  // ---- split-K (one column tile per workgroup): publish, count arrivals, last one
+  // sums the slices in order
+  if (CT == 1 && S > 1) {
     const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
     store_partial(part, ((int64_t)s * a.NT + nt) * 64 + lane, tot);
     wait_stores_performed();
@@ -243,6 +299,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
   }
 
   // ---- epilogue: lane holds D[4g + j][r] = y[m = 4g + j, n]
+  const int n = (nt + cw) * kTileN + r;
   if (n >= a.N) return;
   float sw = 0.0f;
   if (SCH == kW8A8 && !a.out_acc) sw = a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n];
@@ -265,7 +322,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmArgs a, int S, 
 
 template <int QT, int SCH, int NW>
 hipError_t launch_small_w(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-  if (a.fast)
+  if (p.ct != 1) {
+    // several column tiles per workgroup: planned for the aligned path without K slices only
+    if (!a.fast || p.S != 1) return hipErrorInvalidValue;
+    if (p.ct == 2)
+      gemm_small_kernel<QT, SCH, true, NW, 2><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+    else if (p.ct == 4)
+      gemm_small_kernel<QT, SCH, true, NW, 4><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+    else
+      return hipErrorInvalidValue;
+  } else if constexpr (SCH == kW8A8 && QT == kFp8 && NW == 16) {
+    return hipErrorInvalidValue;   // one FP8 W8A8 tile stops at 8 waves (16 would spill)
+  } else if (a.fast)
     gemm_small_kernel<QT, SCH, true, NW><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
   else
     gemm_small_kernel<QT, SCH, false, NW><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
