@@ -80,3 +80,31 @@ def test_family_statistics(tmp_path, capsys):
     _write(p, TRACE_COLS, rows)
     ps.family(str(p), r"gemm_mfma_kernel<0, 0")
     assert "family_mean_us: 20.000" in capsys.readouterr().out
+
+
+def test_counter_ratios_over_passes(tmp_path, capsys):
+    """Ratios of counters collected in separate passes of the same program: latencies as
+    level / requests, hit rate, and reads in flight per wave by Little's law."""
+    def pas(name, counters):
+        rows = [{"Dispatch_Id": 1, "Kernel_Name": K, "Grid_Size": 512 * 172, "Workgroup_Size": 512,
+                 "Counter_Name": n, "Counter_Value": v, "Start_Timestamp": 0, "End_Timestamp": 10000}
+                for n, v in counters]
+        p = tmp_path / name
+        _write(p, PMC_COLS, rows)
+        return str(p)
+    # 1376 waves, 137600 reads (100 per wave) of 480 cycles each over 10 us = 24000 cycles: 2.0 in flight
+    a = pas("a.csv", (("VmemLatency", 480.0), ("SQ_INSTS_VMEM_RD", 137600.0), ("SQ_WAVES", 1376.0)))
+    b = pas("b.csv", (("TCP_TCC_READ_REQ_LATENCY_sum", 3000.0), ("TCP_TCC_READ_REQ_sum", 10.0),
+                      ("TCC_HIT_sum", 3.0), ("TCC_MISS_sum", 1.0), ("TCC_EA0_RDREQ_LEVEL_sum", 800.0),
+                      ("TCC_EA0_RDREQ_sum", 2.0)))
+    ps.counters([a, b], "gemm_mfma", brief=True)
+    line = [l for l in capsys.readouterr().out.splitlines() if l.startswith("gemm_mfma_kernel")][0]
+    f = [x.strip() for x in line.split("|")]
+    assert f[1] == "172 x 512" and int(f[2]) == 2 and float(f[3]) == 10.0
+    r = dict(x.rsplit(" ", 1) for x in f[4].split("; "))
+    assert float(r["vmem latency (cycles)"]) == 480.0
+    assert float(r["L1->L2 read latency (cycles)"]) == 300.0
+    assert float(r["L2 hit %"]) == 75.0
+    assert float(r["L2->fabric read latency (cycles)"]) == 400.0
+    assert float(r["vmem reads in flight per wave"]) == 2.0
+    assert "TCC_HIT_sum" not in f[5] and "SQ_WAVES 1376" in f[5]

@@ -4,6 +4,7 @@
     python -m weight_quantized_linear_qlinear_amd.profile_summary family TRACE.csv REGEX
     python -m weight_quantized_linear_qlinear_amd.profile_summary mfma COUNTERS.csv AGENT_INFO.csv [--match RE]
     python -m weight_quantized_linear_qlinear_amd.profile_summary traffic FETCH.csv WRITE.csv [--match RE]
+    python -m weight_quantized_linear_qlinear_amd.profile_summary counters PASS.csv [PASS.csv ...] [--match RE] [--brief]
 
 `kernels` reads a `--kernel-trace` CSV and prints, per kernel and launch size
 (workgroups), the call count and the duration's mean, p10, p50, p90, min and max;
@@ -14,6 +15,14 @@ kernel and launch size the MFMA utilisation: the matrix-pipe busy cycles over al
 SIMDs divided by the SIMD count times the GPU-active cycles of one XCD
 (GRBM_GUI_ACTIVE is summed over the XCDs), plus the MFMA FLOPs the MOPS counters
 report when they were collected.
+
+`counters` reads any number of `--pmc` CSVs (one pass each) and prints per kernel and
+launch size each counter's mean per dispatch, plus the ratios whose counters are present:
+the mean vector-memory instruction latency (VmemLatency, cycles), the mean L1->L2 read
+latency (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ, cycles), the L2 hit rate, the mean
+L2->fabric read latency (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, cycles), the vector-memory
+reads a wave keeps in flight on average (Little's law) and the L1 address translation miss
+rate.
 
 `traffic` reads one FETCH_SIZE and one WRITE_SIZE run (KiB per dispatch) and prints
 per kernel and launch size the bytes between the L2s and the fabric (the 256 MB
@@ -158,6 +167,58 @@ def traffic(fetch_path: str, write_path: str, match: str | None):
         print(f"dispatches: {n_all}")
 
 
+_RATIOS = [
+    ("vmem latency (cycles)", lambda c: c.get("VmemLatency")),
+    ("L1->L2 read latency (cycles)", lambda c: c["TCP_TCC_READ_REQ_LATENCY_sum"] / c["TCP_TCC_READ_REQ_sum"]
+     if c.get("TCP_TCC_READ_REQ_sum") else None),
+    ("L2 hit %", lambda c: 100 * c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+     if c.get("TCC_HIT_sum", 0) + c.get("TCC_MISS_sum", 0) > 0 else None),
+    ("L2->fabric read latency (cycles)", lambda c: c["TCC_EA0_RDREQ_LEVEL_sum"] / c["TCC_EA0_RDREQ_sum"]
+     if c.get("TCC_EA0_RDREQ_sum") else None),
+    # Little's law: read instructions per wave x their mean latency / the dispatch's cycles
+    # (its duration at 2.4 GHz; GRBM_GUI_ACTIVE also counts the profiler's window around
+    # short dispatches)
+    ("vmem reads in flight per wave", lambda c: c["VmemLatency"] * c["SQ_INSTS_VMEM_RD"] / c["SQ_WAVES"] /
+     (c["_us"] * 2400.0) if c.get("VmemLatency") and c.get("SQ_WAVES") else None),
+    ("L1 translation miss %", lambda c: 100 * c["TCP_UTCL1_TRANSLATION_MISS_sum"] /
+     (c["TCP_UTCL1_TRANSLATION_MISS_sum"] + c["TCP_UTCL1_TRANSLATION_HIT_sum"])
+     if c.get("TCP_UTCL1_TRANSLATION_MISS_sum", 0) + c.get("TCP_UTCL1_TRANSLATION_HIT_sum", 0) > 0 else None),
+]
+
+
+def counters(paths, match: str | None, brief: bool = False):
+    """Per kernel and launch size: mean of every counter per dispatch over all passes,
+    and the ratios above (each pass is a separate run of the same program, so a kernel's
+    dispatches line up by their order within the kernel and launch size)."""
+    groups = collections.defaultdict(lambda: collections.defaultdict(list))
+    us = collections.defaultdict(list)
+    for path in paths:
+        for d in _pivot(path, match).values():
+            key = (short_name(d["name"]), d["wgs"], d["wg"])
+            for k, v in d.items():
+                if k not in ("name", "wgs", "wg", "us"):
+                    groups[key][k].append(v)
+            us[key].append(d["us"])
+    print("# kernel | workgroups x threads | dispatches (all passes) | us per dispatch (under the profiler) | "
+          "ratios | counter means per dispatch")
+    for key, cs in sorted(groups.items(), key=lambda kv: -sum(us[kv[0]])):
+        mean = {k: float(np.mean(v)) for k, v in cs.items()}
+        mean["_us"] = float(np.mean(us[key]))
+        ratios = []
+        for label, f in _RATIOS:
+            try:
+                r = f(mean)
+            except (KeyError, ZeroDivisionError):
+                r = None
+            if r is not None:
+                ratios.append(f"{label} {r:.1f}")
+        keep = ("MeanOccupancyPerCU", "SQ_WAVES", "SQ_INSTS_VMEM_RD")
+        raw = ", ".join(f"{k} {v:.4g}" for k, v in sorted(mean.items())
+                        if not k.startswith("_") and (not brief or k in keep))
+        name, wgs, wg = key
+        print(f"{name} | {wgs} x {wg} | {len(us[key])} | {np.mean(us[key]):.2f} | {'; '.join(ratios)} | {raw}")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -171,6 +232,10 @@ def main(argv=None):
     m.add_argument("counters")
     m.add_argument("agent_info")
     m.add_argument("--match")
+    c = sub.add_parser("counters")
+    c.add_argument("passes", nargs="+")
+    c.add_argument("--match")
+    c.add_argument("--brief", action="store_true", help="ratios, occupancy, waves and read instructions only")
     t = sub.add_parser("traffic")
     t.add_argument("fetch")
     t.add_argument("write")
@@ -182,6 +247,8 @@ def main(argv=None):
         family(a.trace, a.match)
     elif a.cmd == "mfma":
         mfma(a.counters, a.agent_info, a.match)
+    elif a.cmd == "counters":
+        counters(a.passes, a.match, a.brief)
     else:
         traffic(a.fetch, a.write, a.match)
 
