@@ -374,3 +374,31 @@ def test_noalloc_call_validates_on_the_host():
     assert qlq.gemm_plan("w8a16", 2048, 11008, 2048, "int8")["workspace_bytes"] > 32 * 1024 * 1024 + 4096
     st, msg = _status(f, FAKE, 2048, 11008, 2048, FAKE, FAKE, 2048, 0, FAKE, None)
     assert st == 1 and "scratch" in msg
+
+
+def test_small_m_column_tile_plans_keep_their_invariants():
+    """Small-M plans over a grid of decode shapes: several 16-column tiles per workgroup
+    only on the aligned path (K a multiple of 64) without K slices, the grid is one
+    workgroup per group of tiles (and K slice), FP8 W8A8 stays at 8 waves with one or
+    two tiles, and wide outputs at M = 16 take several tiles for every scheme."""
+    wide = set()
+    for sch in ("w8a16", "w8a8_static"):
+        for qt in ("int8", "fp8_e4m3fn"):
+            for M in (1, 2, 5, 6, 8, 12, 16):
+                for K in (64, 100, 704, 2048, 4096, 11008, 14336):
+                    for N in (100, 2048, 5120, 5177, 10240, 11008, 14336, 28672):
+                        p = qlq.gemm_plan(sch, M, K, N, qt)
+                        assert p["kind"] == 0, (sch, qt, M, K, N, p)
+                        ct = p["tile_n"] // 16
+                        assert ct in (1, 2, 4) and p["tile_n"] == 16 * ct
+                        assert p["waves"] in (4, 8, 16)
+                        NT = -(-N // 16)
+                        assert p["grid"] == -(-NT // ct) * p["split_k"], (sch, qt, M, K, N, p)
+                        if ct > 1:
+                            assert p["split_k"] == 1 and K % 64 == 0, (sch, qt, M, K, N, p)
+                            assert NT >= 320 and M >= (6 if sch == "w8a16" else 12)
+                            if M == 16 and K == 2048 and N == 11008:
+                                wide.add((sch, qt))
+                        if sch == "w8a8_static" and qt == "fp8_e4m3fn" and ct < 4:
+                            assert p["waves"] <= 8, (M, K, N, p)
+    assert len(wide) == 4, wide
