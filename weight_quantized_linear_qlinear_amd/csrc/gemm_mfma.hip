@@ -466,45 +466,108 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
   };
   if constexpr (SPLIT) {
     const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
-    const int64_t mine = ((int64_t)s * tiles_m * tiles_n + tile_id) * NV * NT;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) store_partial(part, mine + ((i * TN + j) * 4 + v) * NT + tid, acc_vec(i, j, v));
-    wait_stores_performed();
-    __shared__ uint32_t s_prev;
-    __syncthreads();
-    if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
-    __syncthreads();
-    if (s_prev != (uint32_t)(S - 1)) return;
-    // Sum the slices in slice order 0..S-1 (independent of which workgroup
-    // arrived last, so the fp32 result is deterministic); each slice's values
-    // are loaded together, straight into the accumulator registers.
     const int64_t slice = (int64_t)tiles_m * tiles_n * NV * NT;
     const int64_t base = (int64_t)tile_id * NV * NT;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        accf[i][j] = (f32x16){};
-        acci[i][j] = (i32x16){};
+    __shared__ uint32_t s_prev;
+    // With at most four slices, a workgroup that finds every other slice of its tile
+    // already arrived is the last one: it publishes nothing and adds its own slice
+    // from registers.  Otherwise it publishes its partials, arrives, and the last to
+    // arrive sums (its own slice still from registers).  Tiles with more than 16
+    // vectors per thread (or 8 with eight waves) have no registers for a second copy
+    // of the tile (their main loop would lose registers to it): they read their own
+    // slice back.  Measured on the 3B stack's shapes: the check costs every workgroup
+    // a round trip, which pays with two to four slices but not with seven.
+    constexpr bool kEarlyLast = NV <= 16 && (NW == 4 || NV <= 8);
+    bool own_in_regs = false;
+    if constexpr (kEarlyLast) {
+      if (S <= 4) {
+        if (tid == 0) s_prev = peek_arrivals(&a.counters[tile_id]);
+        __syncthreads();
+        own_in_regs = s_prev == (uint32_t)(S - 1);
       }
-    for (int q = 0; q < S; ++q) {
+    }
+    if (!own_in_regs) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f32x4 p = load_partial(part, base + q * slice + ((i * TN + j) * 4 + v) * NT + tid);
+          for (int v = 0; v < 4; ++v)
+            store_partial(part, base + s * slice + ((i * TN + j) * 4 + v) * NT + tid, acc_vec(i, j, v));
+      wait_stores_performed();
+      __syncthreads();
+      if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
+      __syncthreads();
+      if (s_prev != (uint32_t)(S - 1)) return;
+    }
+    // Sum the slices in slice order 0..S-1 from +0 (independent of which workgroup
+    // is last, so the result is deterministic), each slice's values loaded together;
+    // with kEarlyLast slice s comes from registers.
+    if constexpr (!kEarlyLast) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (T::kIntAcc) acci[i][j][4 * v + e] += __builtin_bit_cast(i32x4, p)[e];
-              else accf[i][j][4 * v + e] += p[e];
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          accf[i][j] = (f32x16){};
+          acci[i][j] = (i32x16){};
+        }
+      for (int q = 0; q < S; ++q) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const f32x4 p = load_partial(part, base + q * slice + ((i * TN + j) * 4 + v) * NT + tid);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (T::kIntAcc) acci[i][j][4 * v + e] += __builtin_bit_cast(i32x4, p)[e];
+                else accf[i][j][4 * v + e] += p[e];
+              }
             }
-          }
+      }
+    } else {
+      f32x16 sumf[TM][TN];
+      i32x16 sumi[TM][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          sumf[i][j] = (f32x16){};
+          sumi[i][j] = (i32x16){};
+        }
+      for (int q = 0; q < S; ++q) {
+        if (q == s) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              if constexpr (T::kIntAcc) sumi[i][j] += acci[i][j];
+              else sumf[i][j] += accf[i][j];
+            }
+          continue;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const f32x4 p = load_partial(part, base + q * slice + ((i * TN + j) * 4 + v) * NT + tid);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (T::kIntAcc) sumi[i][j][4 * v + e] += __builtin_bit_cast(i32x4, p)[e];
+                else sumf[i][j][4 * v + e] += p[e];
+              }
+            }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          accf[i][j] = sumf[i][j];
+          acci[i][j] = sumi[i][j];
+        }
     }
     if (tid == 0) reset_counter(&a.counters[tile_id]);
   }
