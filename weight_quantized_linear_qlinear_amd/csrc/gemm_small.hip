@@ -284,15 +284,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     prev = __shfl(prev, 0, 64);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (prev != (uint32_t)(S - 1)) return;
-    // slices summed in order 0..S-1, whichever workgroup arrived last
+    // slices summed in order 0..S-1, whichever workgroup arrived last (its own slice
+    // from registers: one memory round trip less)
     if constexpr (T::kIntAcc) {
       i32x4 t = {0, 0, 0, 0};
       for (int q = 0; q < S; ++q)
-        t += __builtin_bit_cast(i32x4, load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane));
+        t += __builtin_bit_cast(i32x4, q == s ? tot : load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane));
       tot = __builtin_bit_cast(f32x4, t);
     } else {
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < S; ++q) t += load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane);
+      for (int q = 0; q < S; ++q) t += q == s ? tot : load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane);
       tot = t;
     }
     if (lane == 0) reset_counter(&a.counters[nt]);
