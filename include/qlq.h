@@ -211,8 +211,8 @@ qlq_status qlq_qlinear_w8a8_static_requant(const void* xq, float input_scale,
  * outputs), as one call.  The codes go through the workspace: one quantization
  * pass writes them, the GEMM reads them.  (Quantizing inside the GEMM kernels
  * measured slower on MI355X: the small-M kernel would divide every x element
- * once per 16-column tile, and bf16 x tiles would double the bytes each CU
- * streams through the large-M main loop.)  Size the workspace with
+ * once per workgroup of 16 to 64 output columns, and bf16 x tiles would double
+ * the bytes each CU streams through the large-M main loop.)  Size the workspace with
  * qlq_workspace_bytes(QLQ_SCHEME_W8A8_STATIC_FUSED, ...); it follows the same
  * zero-fill rule as every other workspace. */
 qlq_status qlq_qlinear_w8a8_static_fused(const void* x_bf16, float input_scale,
@@ -292,10 +292,10 @@ qlq_status qlq_kv_dequantize(const void* k_codes, const void* k_scales, const vo
 
 /* The launch plan a GEMM call takes for these sizes when x is 16-byte aligned (what
  * the tests use to show which kernel configuration a case reaches).  kind 0 is the
- * small-M family (M <= 16; tile_m = 16, tile_n = 16, 32 or 64 columns per workgroup,
- * `waves` waves per workgroup), 1 the
- * register-staged large-M kernel (K not a multiple of 64), 2 the direct-to-LDS
- * large-M kernel with tile configuration `cfg` (-1 otherwise).  split_k is the
+ * small-M family (M <= 16; tile_m = 16, tile_n = 16, 32 or 64 columns per
+ * workgroup, `waves` waves per workgroup), 1 the register-staged large-M kernel
+ * (K not a multiple of 64), 2 the direct-to-LDS large-M kernel with tile
+ * configuration `cfg` (-1 otherwise).  split_k is the
  * number of K slices per output tile, grid the workgroups launched and
  * workspace_bytes what the call needs (0 without split-K).  Host only: nothing is
  * enqueued.  Errors as for the GEMM calls' size and enum checks. */
