@@ -15,9 +15,10 @@ from tests.gpu_util import bf16_bits, bf16_to_gpu, bits_to_f64, check_close, f32
 
 pytestmark = pytest.mark.gpu
 
+# the last shape takes several 16-column tiles per small-M workgroup (the bias epilogue per tile)
 SHAPES = [(1, 64, 16), (3, 100, 37), (16, 2048, 2048), (13, 1000, 300), (17, 640, 200), (64, 128, 4096),
           (255, 1024, 136), (257, 320, 250), (256, 2048, 1024), (130, 4096, 96), (37, 1000, 300),
-          (300, 100, 1100)]
+          (300, 100, 1100), (13, 704, 10338)]
 
 
 def _case(seed, M, K, N, qtype, scheme):
