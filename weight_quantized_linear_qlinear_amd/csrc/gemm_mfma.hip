@@ -469,41 +469,28 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_mfma_kerne
     const int64_t slice = (int64_t)tiles_m * tiles_n * NV * NT;
     const int64_t base = (int64_t)tile_id * NV * NT;
     __shared__ uint32_t s_prev;
-    // With at most four slices, a workgroup that finds every other slice of its tile
-    // already arrived is the last one: it publishes nothing and adds its own slice
-    // from registers.  Otherwise it publishes its partials, arrives, and the last to
-    // arrive sums (its own slice still from registers).  Tiles with more than 16
-    // vectors per thread (or 8 with eight waves) have no registers for a second copy
-    // of the tile (their main loop would lose registers to it): they read their own
-    // slice back.  Measured on the 3B stack's shapes: the check costs every workgroup
-    // a round trip, which pays with two to four slices but not with seven.
-    constexpr bool kEarlyLast = NV <= 16 && (NW == 4 || NV <= 8);
-    bool own_in_regs = false;
-    if constexpr (kEarlyLast) {
-      if (S <= 4) {
-        if (tid == 0) s_prev = peek_arrivals(&a.counters[tile_id]);
-        __syncthreads();
-        own_in_regs = s_prev == (uint32_t)(S - 1);
-      }
-    }
-    if (!own_in_regs) {
+    // Publish, arrive, and the last to arrive sums.  Tiles with at most 16
+    // accumulator vectors per thread (8 with eight waves) add the last workgroup's
+    // own slice from registers instead of reading it back; larger tiles have no
+    // registers for the second copy of the tile this takes (their main loop would
+    // lose registers to it).
+    constexpr bool kOwnInRegs = NV <= 16 && (NW == 4 || NV <= 8);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            store_partial(part, base + s * slice + ((i * TN + j) * 4 + v) * NT + tid, acc_vec(i, j, v));
-      wait_stores_performed();
-      __syncthreads();
-      if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
-      __syncthreads();
-      if (s_prev != (uint32_t)(S - 1)) return;
-    }
+        for (int v = 0; v < 4; ++v)
+          store_partial(part, base + s * slice + ((i * TN + j) * 4 + v) * NT + tid, acc_vec(i, j, v));
+    wait_stores_performed();
+    __syncthreads();
+    if (tid == 0) s_prev = arrive(&a.counters[tile_id]);
+    __syncthreads();
+    if (s_prev != (uint32_t)(S - 1)) return;
     // Sum the slices in slice order 0..S-1 from +0 (independent of which workgroup
     // is last, so the result is deterministic), each slice's values loaded together;
-    // with kEarlyLast slice s comes from registers.
-    if constexpr (!kEarlyLast) {
+    // with kOwnInRegs slice s comes from registers.
+    if constexpr (!kOwnInRegs) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -258,12 +258,6 @@ __device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The number of workgroups that have arrived so far (each after its partial stores
-// were performed).
-__device__ __forceinline__ uint32_t peek_arrivals(uint32_t* counter) {
-  return __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ void reset_counter(uint32_t* counter) {
   __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
