@@ -379,9 +379,9 @@ def test_noalloc_call_validates_on_the_host():
 def test_small_m_column_tile_plans_keep_their_invariants():
     """Small-M plans over a grid of decode shapes: several 16-column tiles per workgroup
     only on the aligned path (K a multiple of 64) without K slices and from 320 column
-    tiles (below M = 6 / 12 only for W8A16 with 4096 <= K < 8192), the grid is one
-    workgroup per group of tiles (and K slice), FP8 W8A8 stays at 8 waves with one or
-    two tiles, and wide outputs at M = 16 take several tiles for every scheme."""
+    tiles (below M = 6 / 12 only with 4096 <= K < 8192), the grid is one
+    workgroup per group of tiles (and K slice), W8A8 stays at 8 waves with two tiles (FP8
+    with one too), and wide outputs at M = 16 take several tiles for every scheme."""
     wide = set()
     for sch in ("w8a16", "w8a8_static"):
         for qt in ("int8", "fp8_e4m3fn"):
@@ -397,10 +397,10 @@ def test_small_m_column_tile_plans_keep_their_invariants():
                         assert p["grid"] == -(-NT // ct) * p["split_k"], (sch, qt, M, K, N, p)
                         if ct > 1:
                             assert p["split_k"] == 1 and K % 64 == 0, (sch, qt, M, K, N, p)
-                            k_mid = sch == "w8a16" and 4096 <= K < 8192
+                            k_mid = 4096 <= K < 8192
                             assert NT >= 320 and (M >= (6 if sch == "w8a16" else 12) or k_mid)
                             if M == 16 and K == 2048 and N == 11008:
                                 wide.add((sch, qt))
-                        if sch == "w8a8_static" and qt == "fp8_e4m3fn" and ct < 4:
+                        if sch == "w8a8_static" and (ct == 2 or (qt == "fp8_e4m3fn" and ct == 1)):
                             assert p["waves"] <= 8, (M, K, N, p)
     assert len(wide) == 4, wide

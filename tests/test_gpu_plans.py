@@ -49,9 +49,9 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (13, 64, 10338),    # 4 x 4 / 2 x 4 / 4 x 4
                      (14, 704, 10338),   # 4 x 8 / 2 x 8 / 4 x 4
                      (12, 1024, 10338),  # 4 x 16 / 2 x 8 / 4 x 8
-                     (13, 1984, 5177),   # 2 x 16 / 2 x 16 / 2 x 8
-                     (13, 1984, 10338),  # 4 x 16 / 2 x 16 / 4 x 16
-                     (2, 4160, 5177)]    # W8A16 2 tiles at M = 2 (K from 4096 to 8192)
+                     (13, 1984, 5177),   # 2 x 16 / 2 x 8 / 2 x 8
+                     (13, 1984, 10338),  # 4 x 16 / 2 x 8 / 4 x 16
+                     (2, 4160, 5177)]    # 2 x 16 / 2 x 8 / 2 x 8 at M = 2 (K from 4096 to 8192)
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

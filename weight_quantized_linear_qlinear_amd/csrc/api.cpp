@@ -186,7 +186,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     //    share of the unit's loads: two tiles from 320 column tiles on (W8A16 from
     //    M = 6, W8A8 from M = 12), four from 640 (W8A16 from M = 8, FP8 W8A8 from
     //    M = 12; INT8 W8A8 never gained from four).  Their waves are chosen for
-    //    about 14 per CU (FP8 W8A8 with two tiles: at most 8 waves).
+    //    about 14 per CU (W8A8 with two tiles: at most 8 waves).
     // Over that sweep the rule is within 3.3 % of the best plan per shape (in
     // total; single measurements vary by about 2 %) and 20 % (W8A16) / 6 % (INT8
     // W8A8) / 4 % (FP8 W8A8) faster than the first rule alone.
@@ -208,23 +208,23 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
       while (W > 4 && NT * W > cap * 256) W /= 2;
       const int64_t m2 = scheme == kW8A16 ? 6 : 12;                      // rows for two tiles
       const int64_t m4 = scheme == kW8A16 ? 8 : (TPU == 2 ? 12 : M + 1);  // rows for four
-      // W8A16 with 4096 <= K < 8192 takes two tiles at any M (each unit's two x loads
-      // then serve both) unless that spreads the workgroups worse over the 256 CUs:
-      // every workgroup has the same work, so the busiest CU (ceil(g / 256) of g
-      // workgroups) against the mean (g / 256) sets the time.  Measured at M = 1-4:
-      // 2-12 % faster on 5504, 6144 and 14336 outputs (equal spread), slower on 11008
-      // and 28672 (one tile spreads better); one tile as fast or faster at K = 2048
-      // and 8192.
+      // With 4096 <= K < 8192, two tiles at any M (each unit's x loads then serve
+      // both) unless that spreads the workgroups worse over the 256 CUs: every
+      // workgroup has the same work, so the busiest CU (ceil(g / 256) of g
+      // workgroups) against the mean (g / 256) sets the time.  Measured below the M
+      // thresholds above: 2-12 % faster on 5504, 6144, 8192, 14336 and 16384 outputs
+      // (equal spread), slower on 11008 and 28672 (one tile spreads better); at K =
+      // 2048 (mixed, up to 6 % either way) and 8192 (slower) one tile stays.
       auto spread = [](int64_t g) {
         const double r = (double)g / 256.0;
         return std::ceil(r) / r;
       };
-      const bool k_mid = scheme == kW8A16 && K >= 4096 && K < 8192 && spread(cdiv(NT, 2)) <= spread(NT) + 1e-9;
+      const bool k_mid = K >= 4096 && K < 8192 && spread(cdiv(NT, 2)) <= spread(NT) + 1e-9;
       if (fast && M >= m4 && NT >= 640) ct = 4;
       else if (fast && (M >= m2 || k_mid) && NT >= 320) ct = 2;
       if (ct > 1) {
         const int64_t groups = cdiv(NT, ct);
-        const int64_t w_max = (ct == 2 && TPU == 2) ? 8 : 16;
+        const int64_t w_max = (ct == 2 && scheme == kW8A8) ? 8 : 16;
         double best = 1e300;
         for (int64_t w = 4; w <= w_max; w *= 2) {
           if (w > 4 && w > KU) break;
