@@ -59,7 +59,9 @@ def test_packed_bytes_is_tile_padded_and_about_half_of_bf16():
 def test_workspace_sizes():
     assert qlq.workspace_bytes("w8a16", 16, 2048, 11008, "fp8_e4m3fn") == 0      # enough column blocks
     assert qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8") == 0              # waves split K in one workgroup
-    assert qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8") > 0               # narrow N: split over K
+    assert qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8") == 0              # narrow N, 32 units of K: one slice
+    assert qlq.workspace_bytes("w8a16", 1, 14336, 1024, "int8") > 0              # narrow N, deep K: split over K
+    assert qlq.workspace_bytes("w8a16", 1, 13824, 5120, "int8") > 0              # 320 column tiles, deep K: split
     assert qlq.workspace_bytes("w8a8_static", 1024, 2048, 11008, "fp8_e4m3fn") == 0
     assert qlq.workspace_bytes("w8a8_static", 256, 11008, 2048, "int8") > 0
     assert qlq.workspace_bytes("w8a16", 0, 64, 64, "int8") == 0
@@ -104,10 +106,11 @@ def test_validation_enums_scales_and_workspace():
     st, msg = _status(L.qlq_qlinear_w8a8_static, FAKE, 1.0, 4, 133145, 16, FAKE, FAKE, 16, 0, 0, FAKE, None, 0, None)
     assert st == 1 and "133144" in msg
     # a split-K plan needs its workspace
-    need = qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8")
-    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 1024, FAKE, FAKE, 1024, 0, FAKE, None, 0, None)
+    need = qlq.workspace_bytes("w8a16", 1, 14336, 1024, "int8")
+    assert need > 0
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 14336, 1024, FAKE, FAKE, 1024, 0, FAKE, None, 0, None)
     assert st == 1 and "workspace" in msg
-    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 2048, 1024, FAKE, FAKE, 1024, 0, FAKE, FAKE, need - 1, None)
+    st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 14336, 1024, FAKE, FAKE, 1024, 0, FAKE, FAKE, need - 1, None)
     assert st == 1 and "workspace" in msg
     # misaligned packed weights
     st, msg = _status(L.qlq_qlinear_w8a16, FAKE, 1, 64, 16, ctypes.c_void_p(0x10008), FAKE, 16, 0, FAKE, None, 0,
@@ -404,3 +407,45 @@ def test_small_m_column_tile_plans_keep_their_invariants():
                         if sch == "w8a8_static" and (ct == 2 or (qt == "fp8_e4m3fn" and ct == 1)):
                             assert p["waves"] <= 8, (M, K, N, p)
     assert len(wide) == 4, wide
+
+
+def test_small_m_k_slice_plans_keep_their_invariants():
+    """K slices of small-M plans: narrow outputs (fewer than 128 column tiles) take about
+    64 units of 64 inputs per slice (48 two-tile units for FP8 W8A8, 32 for W8A16 above
+    M = 8) on at most 256 workgroups; 128 to 191 tiles take two slices over 64 units or more; wider outputs
+    are split only with one column tile per workgroup, 257 to 1024 tiles, deep weights
+    (128 units; FP8 W8A8 96 two-tile units) and the busiest CU above 1.2 times the mean,
+    into the 2 to 4 slices with the best spread (four waves each)."""
+    def cdiv(a, b):
+        return -(-a // b)
+
+    def spread(g):
+        return cdiv(g, 256) / (g / 256)
+
+    for sch in ("w8a16", "w8a8_static"):
+        for qt in ("int8", "fp8_e4m3fn"):
+            tpu = 2 if (sch == "w8a8_static" and qt == "fp8_e4m3fn") else 1
+            for M in (1, 4, 8, 16):
+                for K in (100, 2048, 4096, 8192, 11008, 13824, 14336, 28672, 100000):
+                    for N in (16, 100, 1024, 2047, 2048, 3000, 4100, 5120, 6144, 11008, 16400, 17000):
+                        p = qlq.gemm_plan(sch, M, K, N, qt)
+                        NT, KU = cdiv(N, 16), cdiv(cdiv(K, 64), tpu)
+                        S, ct = p["split_k"], p["tile_n"] // 16
+                        where = (sch, qt, M, K, N, p)
+                        assert 1 <= S <= KU and S * NT <= 1024 * 256, where
+                        if S > 1:
+                            assert p["workspace_bytes"] >= S * NT * 1024, where
+                        if NT < 128:
+                            target = 48 if tpu == 2 else (32 if sch == "w8a16" and M > 8 else 64)
+                            s0 = max(1, min(cdiv(256, NT), cdiv(KU, target)))
+                            assert S == cdiv(KU, cdiv(KU, s0)), where      # equal slices of whole units
+                            assert cdiv(KU, S) <= target or S * NT >= 256, where
+                        elif NT < 192:
+                            assert S == (2 if KU >= 64 else 1), where
+                        elif S > 1:
+                            assert ct == 1 and 256 < NT <= 1024 and KU >= (96 if tpu == 2 else 128), where
+                            assert spread(NT) > 1.2 and p["waves"] == 4, where
+                            best = min(range(2, 5), key=lambda s: (round(spread(NT * s), 9), s))
+                            assert S == cdiv(KU, cdiv(KU, best)), where
+                        elif NT > 1024 or KU < (96 if tpu == 2 else 128):
+                            assert S == 1, where

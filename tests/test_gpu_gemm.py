@@ -146,7 +146,7 @@ def test_w8a8_fp8_integer_exact():
 @pytest.mark.parametrize("scheme", ["w8a16", "w8a8_static"])
 def test_split_k_workspace_is_reusable(scheme):
     # repeated split-K calls on one workspace give identical results
-    M, K, N = (1, 2048, 1024) if scheme == "w8a16" else (256, 11008, 256)
+    M, K, N = (1, 8192, 1024) if scheme == "w8a16" else (256, 11008, 256)
     assert qlq.workspace_bytes(scheme, M, K, N, "int8") > 0
     _, calib, x, qw, q_ref, s_ref = _prep(77, M, K, N, "int8")
     xg = bf16_to_gpu(x)
@@ -165,7 +165,7 @@ def test_zero_input_gives_zero_output():
 
 
 def test_hip_graph_replay_matches_eager():
-    M, K, N = 16, 2048, 1024
+    M, K, N = 16, 8192, 1024                    # a split-K plan: its workspace is reused by every replay
     _, _, x, qw, _, _ = _prep(9, M, K, N, "fp8_e4m3fn")
     xg = bf16_to_gpu(x)
     eager = qlq.qlinear_w8a16(xg, qw).clone()
@@ -185,9 +185,9 @@ def test_hip_graph_replay_matches_eager():
 def test_split_k_plans_interleaved_on_one_workspace():
     # Split-K calls with different plans (column-block counts, slice counts, kernel
     # families) alternate on the one shared workspace; each must stay correct.
-    cases = [(1, 2048, 1024, "w8a16", "int8"), (16, 11008, 128, "w8a8_static", "int8"),
-             (1, 4096, 512, "w8a8_static", "fp8_e4m3fn"), (256, 11008, 256, "w8a8_static", "int8"),
-             (13, 1000, 300, "w8a16", "fp8_e4m3fn"), (64, 4096, 512, "w8a16", "int8")]
+    cases = [(1, 8192, 1024, "w8a16", "int8"), (16, 11008, 128, "w8a8_static", "int8"),
+             (1, 8192, 512, "w8a8_static", "fp8_e4m3fn"), (256, 11008, 256, "w8a8_static", "int8"),
+             (13, 5000, 300, "w8a16", "fp8_e4m3fn"), (64, 4096, 512, "w8a16", "int8")]
     prepared = []
     for i, (M, K, N, scheme, qtype) in enumerate(cases):
         assert qlq.workspace_bytes(scheme, M, K, N, qtype) > 0
@@ -213,7 +213,7 @@ def test_split_k_plans_interleaved_on_one_workspace():
                     check_close(acc, ref)
 
 
-@pytest.mark.parametrize("MKN", [(1, 11008, 2048), (256, 11008, 2048), (16, 2048, 1024)])
+@pytest.mark.parametrize("MKN", [(1, 11008, 2048), (256, 11008, 2048), (16, 8192, 1024)])
 def test_split_k_int8_repeated_bit_exact(MKN):
     # Split-K slices may land on different XCDs; the integer accumulators must
     # come out identical to the oracle on every one of many repeated calls.

@@ -51,7 +51,13 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (12, 1024, 10338),  # 4 x 16 / 2 x 8 / 4 x 8
                      (13, 1984, 5177),   # 2 x 16 / 2 x 8 / 2 x 8
                      (13, 1984, 10338),  # 4 x 16 / 2 x 8 / 4 x 16
-                     (2, 4160, 5177)]    # 2 x 16 / 2 x 8 / 2 x 8 at M = 2 (K from 4096 to 8192)
+                     (2, 4160, 5177),    # 2 x 16 / 2 x 8 / 2 x 8 at M = 2 (K from 4096 to 8192)
+                     # K slices x waves for W8A16 / INT8 W8A8 / FP8 W8A8
+                     (1, 8256, 2100),    # 2 x 16 / 2 x 16 / 2 x 8 (fewer than 192 column tiles)
+                     (2, 8192, 4100),    # 4 x 4 / 4 x 4 (257 column tiles, deep K) / 1 x 4
+                     (3, 4160, 3080),    # 1 x 8 / 1 x 16 / 1 x 8
+                     (1, 4224, 16),      # 2 x 8 / 2 x 8 / 1 x 8 (one column tile)
+                     (1, 6464, 16)]      # 2 x 8 / 2 x 8 / 2 x 4
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

@@ -194,14 +194,24 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
     const int64_t KU = cdiv(KT, TPU);
     const int64_t max_waves = TPU == 2 ? 8 : 16;
+    // A third sweep (N 1024 to 8192 with K 4096 to 28672, M 1 / 4 / 8 / 16, every
+    // forced choice of K slices and waves) set the slices of narrow outputs (fewer
+    // than 128 column tiles): about 64 one-tile units per slice (48 of FP8 W8A8's
+    // two-tile units; 32 for W8A16 above M = 8, whose bf16 x then outweighs the
+    // codes), at most 256 workgroups, with the waves that one load batch needs and
+    // no more (N = 1024: K = 4096 unsplit at M <= 8, 6-18 % faster than two slices;
+    // K = 14336 and 28672 in three or four slices, 9-34 % faster).
     int64_t S = 1;
-    if (NT < 128) S = std::min(cdiv(128, NT), std::max<int64_t>(1, KU / kSmallUnitsPerWave));
+    const bool narrow = NT < 128;
+    const int64_t narrow_units = TPU == 2 ? 48 : (scheme == kW8A16 && M > 8 ? 32 : 64);
+    if (narrow) S = std::max<int64_t>(1, std::min(cdiv(256, NT), cdiv(KU, narrow_units)));
     else if (NT < 192 && KU >= 64) S = 2;
-    const int64_t ups = cdiv(KU, S);
+    int64_t ups = cdiv(KU, S);
     S = cdiv(KU, ups);
     int64_t W = 4;
     while (W < max_waves && cdiv(ups, W) > kSmallUnitsPerWave) W *= 2;
-    while (W < max_waves && NT * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
+    if (!narrow)
+      while (W < max_waves && NT * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
     int64_t ct = 1;
     if (S == 1) {
       const int64_t cap = scheme == kW8A16 ? 12 : 24;           // waves per CU
@@ -235,6 +245,24 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
           }
         }
       }
+      // One column tile per workgroup over deep weights (at least 128 one-tile or
+      // 96 two-tile units), when 257 to 1024 tiles leave the busiest CU more than 1.2
+      // times the mean: K slices (2 to 4, the best spread, fewest on ties) with four waves.
+      // The third sweep: 320 and 384 column tiles over K = 8192 to 14336 at M <= 8,
+      // 5-15 % faster (13824 -> 5120, 14336 -> 6144); shallower weights on the same
+      // tile counts gained nothing.
+      if (ct == 1 && NT > 256 && NT <= kMaxSplitTiles && KU >= (TPU == 2 ? 96 : 128) && spread(NT) > 1.2 + 1e-9) {
+        int64_t s_best = 2;
+        for (int64_t s = 3; s <= 4; ++s)
+          if (spread(NT * s) < spread(NT * s_best) - 1e-9) s_best = s;
+        ups = cdiv(KU, s_best);
+        S = cdiv(KU, ups);
+        W = 4;
+      }
+      // FP8 W8A8 without slices over K >= 8192 (64 two-tile units) on 256 or more
+      // column tiles: four waves, each looping over several load batches, were 1-7 %
+      // faster than eight in the third sweep.
+      if (ct == 1 && S == 1 && TPU == 2 && NT >= 256 && KU >= 64) W = 4;
     }
     p.S = (int)S;
     p.ct = (int)ct;
@@ -243,7 +271,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     p.waves = (int)W;
     p.tiles = (int)NT;
     p.grid = (int)(cdiv(NT, ct) * S);
-    if (S > 1) {   // S > 1 only when NT < 192 <= kMaxSplitTiles
+    if (S > 1) {   // S > 1 only when NT < 192 or 256 < NT <= kMaxSplitTiles
       p.ws_counter_bytes = kCounterBytes;
       p.ws_bytes = p.ws_counter_bytes + (size_t)S * NT * 64 * 16;
     }
