@@ -59,7 +59,8 @@ def test_packed_bytes_is_tile_padded_and_about_half_of_bf16():
 def test_workspace_sizes():
     assert qlq.workspace_bytes("w8a16", 16, 2048, 11008, "fp8_e4m3fn") == 0      # enough column blocks
     assert qlq.workspace_bytes("w8a16", 1, 2048, 2048, "int8") == 0              # waves split K in one workgroup
-    assert qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8") == 0              # narrow N, 32 units of K: one slice
+    assert qlq.gemm_plan("w8a16", 1, 2048, 1024, "int8")["split_k"] == 1          # narrow N, 32 units of K: one slice
+    assert qlq.workspace_bytes("w8a16", 1, 2048, 1024, "int8") > 0               # (unaligned x: generic path, split)
     assert qlq.workspace_bytes("w8a16", 1, 14336, 1024, "int8") > 0              # narrow N, deep K: split over K
     assert qlq.workspace_bytes("w8a16", 1, 13824, 5120, "int8") > 0              # 320 column tiles, deep K: split
     assert qlq.workspace_bytes("w8a8_static", 1024, 2048, 11008, "fp8_e4m3fn") == 0
@@ -410,9 +411,10 @@ def test_small_m_column_tile_plans_keep_their_invariants():
 
 
 def test_small_m_k_slice_plans_keep_their_invariants():
-    """K slices of small-M plans: narrow outputs (fewer than 128 column tiles) take about
-    64 units of 64 inputs per slice (48 two-tile units for FP8 W8A8, 32 for W8A16 above
-    M = 8) on at most 256 workgroups; 128 to 191 tiles take two slices over 64 units or more; wider outputs
+    """K slices of small-M plans: narrow outputs (fewer than 128 column tiles) on aligned K
+    take about 64 units of 64 inputs per slice (48 two-tile units for FP8 W8A8, 32 for
+    W8A16 above M = 8) on at most 256 workgroups (ragged K: up to 128 workgroups of at
+    least 8 units); 128 to 191 tiles take two slices over 64 units or more; wider outputs
     are split only with one column tile per workgroup, 257 to 1024 tiles, deep weights
     (128 units; FP8 W8A8 96 two-tile units) and the busiest CU above 1.2 times the mean,
     into the 2 to 4 slices with the best spread (four waves each)."""
@@ -435,11 +437,14 @@ def test_small_m_k_slice_plans_keep_their_invariants():
                         assert 1 <= S <= KU and S * NT <= 1024 * 256, where
                         if S > 1:
                             assert p["workspace_bytes"] >= S * NT * 1024, where
-                        if NT < 128:
+                        if NT < 128 and K % 64 == 0:
                             target = 48 if tpu == 2 else (32 if sch == "w8a16" and M > 8 else 64)
                             s0 = max(1, min(cdiv(256, NT), cdiv(KU, target)))
                             assert S == cdiv(KU, cdiv(KU, s0)), where      # equal slices of whole units
                             assert cdiv(KU, S) <= target or S * NT >= 256, where
+                        elif NT < 128:                                       # generic path: the first rule
+                            s0 = min(cdiv(128, NT), max(1, KU // 8))
+                            assert S == cdiv(KU, cdiv(KU, s0)), where
                         elif NT < 192:
                             assert S == (2 if KU >= 64 else 1), where
                         elif S > 1:

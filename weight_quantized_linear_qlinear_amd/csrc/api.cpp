@@ -200,11 +200,15 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // two-tile units; 32 for W8A16 above M = 8, whose bf16 x then outweighs the
     // codes), at most 256 workgroups, with the waves that one load batch needs and
     // no more (N = 1024: K = 4096 unsplit at M <= 8, 6-18 % faster than two slices;
-    // K = 14336 and 28672 in three or four slices, 9-34 % faster).
+    // K = 14336 and 28672 in three or four slices, 9-34 % faster).  That sweep ran
+    // on the aligned path; on the generic one (K % 64 != 0 or x not 16-byte aligned:
+    // per-element bounds checks) the longer slices were 35-50 % slower (5000 -> 300
+    // at M = 8 / 16), so it keeps the first rule's slices.
     int64_t S = 1;
-    const bool narrow = NT < 128;
+    const bool narrow = NT < 128 && fast;
     const int64_t narrow_units = TPU == 2 ? 48 : (scheme == kW8A16 && M > 8 ? 32 : 64);
     if (narrow) S = std::max<int64_t>(1, std::min(cdiv(256, NT), cdiv(KU, narrow_units)));
+    else if (NT < 128) S = std::min(cdiv(128, NT), std::max<int64_t>(1, KU / kSmallUnitsPerWave));
     else if (NT < 192 && KU >= 64) S = 2;
     int64_t ups = cdiv(KU, S);
     S = cdiv(KU, ups);
