@@ -342,20 +342,20 @@ def test_parity_shapes_reach_every_launch_plan():
     so no kernel instantiation the library can launch goes without an oracle comparison.
     A plan is, for large M, the kernel (direct-to-LDS for K a multiple of 64, else
     register-staged), its tile configuration and whether K is split; for small M, the
-    waves per workgroup, the 16-column tiles per workgroup, whether K is split and
-    whether K is a multiple of 64 (the aligned path)."""
+    waves per workgroup, the 16-column tiles per workgroup, whether K is split, whether
+    K is a multiple of 64 (the aligned path) and whether there are several 16-row groups."""
     from tests.test_gpu_gemm import PAIR_SHAPES, SHAPES
     from tests.test_gpu_plans import SMALL_PLAN_SHAPES, W8A16_PLAN_SHAPES, W8A8_PLAN_SHAPES
 
     def key(mkn, p):
         if p["kind"] == 0:
-            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0, p["tile_n"]
+            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0, p["tile_n"], mkn[0] > 16
         return p["kind"], p["cfg"], p["split_k"] > 1
 
     grid = [(M, K, N) for M in range(17, 1100, 48) for K in range(64, 11100, 64 * 7)
             for N in range(100, 15000, 457)]
     grid += [(M, K, N) for M in (17, 300, 1000) for K in (100, 1000, 1727, 5000) for N in (100, 2000, 11000)]
-    grid += [(M, K, N) for M in (1, 2, 5, 16) for K in list(range(64, 16400, 320)) + [100, 1000, 1727]
+    grid += [(M, K, N) for M in (1, 2, 5, 16, 20, 33, 64) for K in list(range(64, 16400, 320)) + [100, 1000, 1727]
              for N in range(16, 15000, 397)]
     for scheme, extra in (("w8a16", W8A16_PLAN_SHAPES), ("w8a8_static", W8A8_PLAN_SHAPES)):
         for qtype in ("int8", "fp8_e4m3fn"):
@@ -408,6 +408,34 @@ def test_small_m_column_tile_plans_keep_their_invariants():
                         if sch == "w8a8_static" and (ct == 2 or (qt == "fp8_e4m3fn" and ct == 1)):
                             assert p["waves"] <= 8, (M, K, N, p)
     assert len(wide) == 4, wide
+
+
+def test_batched_decode_plans_take_row_groups():
+    """From 17 to 64 rows on aligned K, the small-M kernel runs one workgroup per 16-row
+    group when it measured faster than the direct-to-LDS kernel: two groups unless K is
+    12288 or more, three or four only for weights of at most 8M codes; ragged K and larger
+    M keep the large-M kernels.  The grid and workspace count every group, and K slices
+    keep one arrival counter per (group, column tile) inside the counter region."""
+    def cdiv(a, b):
+        return -(-a // b)
+
+    for sch in ("w8a16", "w8a8_static"):
+        for qt in ("int8", "fp8_e4m3fn"):
+            for M in (16, 17, 24, 32, 33, 48, 64, 65, 100):
+                for K in (64, 1000, 2048, 4096, 11008, 12288, 14336):
+                    for N in (16, 1024, 2048, 4096, 11008):
+                        p = qlq.gemm_plan(sch, M, K, N, qt)
+                        where = (sch, qt, M, K, N, p)
+                        nrg = cdiv(M, 16)
+                        small = M <= 16 or (M <= 64 and K % 64 == 0 and
+                                            (K < 12288 if nrg <= 2 else N * K <= 8 << 20))
+                        assert (p["kind"] == 0) == small, where
+                        if p["kind"] != 0:
+                            continue
+                        NT, ct, S = cdiv(N, 16), p["tile_n"] // 16, p["split_k"]
+                        assert p["tile_m"] == 16 and p["grid"] == cdiv(NT, ct) * S * nrg, where
+                        if S > 1:
+                            assert NT * nrg <= 1024 and p["workspace_bytes"] >= S * nrg * NT * 1024, where
 
 
 def test_small_m_k_slice_plans_keep_their_invariants():

@@ -1,6 +1,7 @@
 """Parity of every launch plan the planner chooses (large M: tile configuration, split or
 not; small M: waves per workgroup, 16-column tiles per workgroup, split or not, aligned
-K or not), beyond the ones the small shapes of test_gpu_gemm.py reach.
+K or not, one or several 16-row groups), beyond the ones the small shapes of
+test_gpu_gemm.py reach.
 
 The direct-to-LDS kernel has one instantiation per tile configuration, and the
 loop of each differs (waves per tile, stages, whether a wave copies exactly the
@@ -23,9 +24,9 @@ pytestmark = pytest.mark.gpu
 QTYPES = ["int8", "fp8_e4m3fn"]
 # (M, K, N) -> (tile configuration, split-K) of the W8A16 planner
 W8A16_PLAN_SHAPES = [(257, 64, 11072),    # 128x256, four-stage ring, no split
-                     (17, 6976, 11072),   # 128x256, four-stage ring, K slices
+                     (33, 6720, 11072),   # 128x256, four-stage ring, K slices
                      (257, 640, 11072),   # 128x256, two-stage ring, no split
-                     (17, 6400, 11072),   # 128x256, two-stage ring, K slices
+                     (33, 6272, 11072),   # 128x256, two-stage ring, K slices
                      (769, 256, 14026),   # 256x256, no split
                      (129, 5824, 11072)]  # 256x256, K slices
 # (M, K, N) of the W8A8 planner
@@ -34,7 +35,7 @@ W8A8_PLAN_SHAPES = [(769, 1024, 14026),   # 256x256 eight waves, no split
                     (513, 6976, 13393),   # 256x256 three-stage ring, no split
                     (535, 512, 13175),    # 256x192, no split
                     (129, 9472, 11072),   # 256x192, K slices
-                    (17, 1216, 100)]      # 128x128 four waves, K slices
+                    (65, 960, 16)]        # 128x128 four waves, K slices
 
 
 # (M, K, N) -> small-M plans (waves per workgroup, column tiles per workgroup, K slices,
@@ -57,7 +58,12 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (2, 8192, 4100),    # 4 x 4 / 4 x 4 (257 column tiles, deep K) / 1 x 4
                      (3, 4160, 3080),    # 1 x 8 / 1 x 16 / 1 x 8
                      (1, 4224, 16),      # 2 x 8 / 2 x 8 / 1 x 8 (one column tile)
-                     (1, 6464, 16)]      # 2 x 8 / 2 x 8 / 2 x 4
+                     (1, 6464, 16),      # 2 x 8 / 2 x 8 / 2 x 4
+                     # batched decode: 16-row groups (the last one partial) x slices x waves x tiles
+                     (17, 2112, 16), (17, 4160, 16), (17, 8576, 1014),     # K slices, one column
+                     (17, 64, 5127), (17, 64, 10611), (17, 512, 5127),     # two and four column tiles
+                     (17, 960, 10611), (17, 960, 5127), (33, 4160, 1604),  # up to 16 waves, three groups
+                     (17, 4544, 1014), (17, 4096, 2385), (20, 6464, 16)]    # K slices, 4 / 8 waves
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -66,7 +72,7 @@ def test_w8a16_plan_parity(qtype, MKN):
     M, K, N = MKN
     plan = qlq.gemm_plan("w8a16", M, K, N, qtype)
     print(f"w8a16 {qtype} M={M} K={K} N={N} plan {plan}", flush=True)
-    assert plan["kind"] == (2 if M > 16 else 0)
+    assert plan["kind"] == (0 if MKN in SMALL_PLAN_SHAPES else 2)
     _, _, x, qw, q_ref, s_ref = _prep(4000 + M * 7 + K + N, M, K, N, qtype)
     y = qlq.qlinear_w8a16(bf16_to_gpu(x), qw)
     ref = oracle.qlinear_w8a16(x, q_ref, s_ref, qtype)
@@ -79,7 +85,7 @@ def test_w8a8_plan_parity(qtype, MKN):
     M, K, N = MKN
     plan = qlq.gemm_plan("w8a8_static", M, K, N, qtype)
     print(f"w8a8 {qtype} M={M} K={K} N={N} plan {plan}", flush=True)
-    assert plan["kind"] == (2 if M > 16 else 0)
+    assert plan["kind"] == (0 if MKN in SMALL_PLAN_SHAPES else 2)
     _, calib, x, qw, q_ref, s_ref = _prep(5000 + M * 7 + K + N, M, K, N, qtype)
     sx = oracle.calibrate_input_scale(calib, qtype)
     xq_ref = oracle.quantize_act_static(x, sx, qtype)

@@ -45,6 +45,9 @@ constexpr int64_t kMaxInt8K = 133144;                // 127 * 127 * K < 2^31
 constexpr int64_t kMaxSplitTiles = 1024;
 constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
 constexpr int64_t kSmallUnitsPerWave = 8;   // matches kUnroll of the small-M kernel
+// Batched decode: the small-M kernel takes up to this many rows (16-row groups, aligned
+// path) before the direct-to-LDS kernel's 128-row tiles (see plan_gemm).
+constexpr int64_t kSmallMaxRows = 64;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -163,10 +166,22 @@ GemmPlan plan_mfma(int scheme, int64_t M, int64_t K, int64_t N) {
 }  // namespace
 
 GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool fast) {
-  if (M > 16 && fast && K % 64 == 0) return plan_mfma(scheme, M, K, N);
+  const bool aligned_path = fast && K % 64 == 0;
+  // Batched decode (16 < M <= 64, aligned path): the small-M kernel with one workgroup
+  // per 16-row group (each group re-reads the weights, from L2 when its siblings run
+  // beside it) against the direct-to-LDS kernel, whose 128-row tiles stream 128 rows
+  // of x whatever M is.  Same-box timings (INT8 W8A16, FP8 and INT8 W8A8, stack and
+  // 7-8B shapes): with two groups (M <= 32) the small-M kernel took 0.36-0.85 of the
+  // time (2048 -> 2048: 13.4 -> 4.8 us; 11008 -> 2048: 23.7 -> 19.5) except on deep
+  // weights (14336 -> 4096: 1.11); with three or four only small weights gained
+  // (2048 x 2048 and 4096 -> 1024: 0.4-0.6; 4096 x 4096 1.10, 11008 -> 2048 up to 1.5).
+  bool small = M <= 16;
+  if (!small && aligned_path && M <= kSmallMaxRows)
+    small = cdiv(M, 16) <= 2 ? K < 12288 : N * K <= (int64_t(8) << 20);
+  if (!small && aligned_path) return plan_mfma(scheme, M, K, N);
   GemmPlan p;
   const int64_t KT = cdiv(K, 64), NT = cdiv(N, 16);
-  if (M <= 16) {
+  if (small) {
     // Small-M: one workgroup per 16 output columns, with 4, 8 or 16 waves
     // splitting K inside it (summed through LDS).  Measured on MI355X over
     // decode shapes with N from 2048 to 14336 and K from 2048 to 14336: K splits
@@ -191,6 +206,9 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // total; single measurements vary by about 2 %) and 20 % (W8A16) / 6 % (INT8
     // W8A8) / 4 % (FP8 W8A8) faster than the first rule alone.
     p.kind = 0;
+    // Above 16 rows every 16-row group is a workgroup of its own: the rules below see
+    // a group's rows (Mg) and count workgroups and waves over all NRG groups.
+    const int64_t Mg = std::min<int64_t>(M, 16), NRG = cdiv(M, 16);
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
     const int64_t KU = cdiv(KT, TPU);
     const int64_t max_waves = TPU == 2 ? 8 : 16;
@@ -206,8 +224,8 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // at M = 8 / 16), so it keeps the first rule's slices.
     int64_t S = 1;
     const bool narrow = NT < 128 && fast;
-    const int64_t narrow_units = TPU == 2 ? 48 : (scheme == kW8A16 && M > 8 ? 32 : 64);
-    if (narrow) S = std::max<int64_t>(1, std::min(cdiv(256, NT), cdiv(KU, narrow_units)));
+    const int64_t narrow_units = TPU == 2 ? 48 : (scheme == kW8A16 && Mg > 8 ? 32 : 64);
+    if (narrow) S = std::max<int64_t>(1, std::min(cdiv(256, NT * NRG), cdiv(KU, narrow_units)));
     else if (NT < 128) S = std::min(cdiv(128, NT), std::max<int64_t>(1, KU / kSmallUnitsPerWave));
     else if (NT < 192 && KU >= 64) S = 2;
     int64_t ups = cdiv(KU, S);
@@ -215,13 +233,13 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     int64_t W = 4;
     while (W < max_waves && cdiv(ups, W) > kSmallUnitsPerWave) W *= 2;
     if (!narrow)
-      while (W < max_waves && NT * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
+      while (W < max_waves && NT * NRG * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
     int64_t ct = 1;
     if (S == 1) {
       const int64_t cap = scheme == kW8A16 ? 12 : 24;           // waves per CU
-      while (W > 4 && NT * W > cap * 256) W /= 2;
+      while (W > 4 && NT * NRG * W > cap * 256) W /= 2;
       const int64_t m2 = scheme == kW8A16 ? 6 : 12;                      // rows for two tiles
-      const int64_t m4 = scheme == kW8A16 ? 8 : (TPU == 2 ? 12 : M + 1);  // rows for four
+      const int64_t m4 = scheme == kW8A16 ? 8 : (TPU == 2 ? 12 : Mg + 1);  // rows for four
       // With 4096 <= K < 8192, two tiles at any M (each unit's x loads then serve
       // both) unless that spreads the workgroups worse over the 256 CUs: every
       // workgroup has the same work, so the busiest CU (ceil(g / 256) of g
@@ -233,16 +251,16 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
         const double r = (double)g / 256.0;
         return std::ceil(r) / r;
       };
-      const bool k_mid = K >= 4096 && K < 8192 && spread(cdiv(NT, 2)) <= spread(NT) + 1e-9;
-      if (fast && M >= m4 && NT >= 640) ct = 4;
-      else if (fast && (M >= m2 || k_mid) && NT >= 320) ct = 2;
+      const bool k_mid = K >= 4096 && K < 8192 && spread(cdiv(NT, 2) * NRG) <= spread(NT * NRG) + 1e-9;
+      if (fast && Mg >= m4 && NT >= 640) ct = 4;
+      else if (fast && (Mg >= m2 || k_mid) && NT >= 320) ct = 2;
       if (ct > 1) {
         const int64_t groups = cdiv(NT, ct);
         const int64_t w_max = (ct == 2 && scheme == kW8A8) ? 8 : 16;
         double best = 1e300;
         for (int64_t w = 4; w <= w_max; w *= 2) {
           if (w > 4 && w > KU) break;
-          const double d = std::fabs((double)(groups * w) / 256.0 - 14.0);
+          const double d = std::fabs((double)(groups * NRG * w) / 256.0 - 14.0);
           if (d < best - 1e-9) {
             best = d;
             W = w;
@@ -255,7 +273,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
       // The third sweep: 320 and 384 column tiles over K = 8192 to 14336 at M <= 8,
       // 5-15 % faster (13824 -> 5120, 14336 -> 6144); shallower weights on the same
       // tile counts gained nothing.
-      if (ct == 1 && NT > 256 && NT <= kMaxSplitTiles && KU >= (TPU == 2 ? 96 : 128) && spread(NT) > 1.2 + 1e-9) {
+      if (ct == 1 && NRG == 1 && NT > 256 && NT <= kMaxSplitTiles && KU >= (TPU == 2 ? 96 : 128) && spread(NT) > 1.2 + 1e-9) {
         int64_t s_best = 2;
         for (int64_t s = 3; s <= 4; ++s)
           if (spread(NT * s) < spread(NT * s_best) - 1e-9) s_best = s;
@@ -268,16 +286,22 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
       // faster than eight in the third sweep.
       if (ct == 1 && S == 1 && TPU == 2 && NT >= 256 && KU >= 64) W = 4;
     }
+    // One arrival counter per (row group, column tile): NRG <= 4 keeps every split plan
+    // above (fewer than 192 column tiles, or one row group) within the counter region.
+    if (S > 1 && NT * NRG > kMaxSplitTiles) {
+      S = 1;
+      ups = KU;
+    }
     p.S = (int)S;
     p.ct = (int)ct;
     p.units_per_split = (int)ups;
     p.units_per_wave = (int)cdiv(ups, W);
     p.waves = (int)W;
     p.tiles = (int)NT;
-    p.grid = (int)(cdiv(NT, ct) * S);
+    p.grid = (int)(cdiv(NT, ct) * S * NRG);
     if (S > 1) {   // S > 1 only when NT < 192 or 256 < NT <= kMaxSplitTiles
       p.ws_counter_bytes = kCounterBytes;
-      p.ws_bytes = p.ws_counter_bytes + (size_t)S * NT * 64 * 16;
+      p.ws_bytes = p.ws_counter_bytes + (size_t)S * NRG * NT * 64 * 16;
     }
   } else {
     p.kind = 1;

@@ -1,4 +1,5 @@
-// Small-M (decode, M <= 16) quantized GEMM family.
+// Small-M (decode, M <= 16; batched decode up to 64 rows in 16-row groups) quantized
+// GEMM family.
 //
 // Decode is bound by reading the weights once ("Nano-vLLM-MoE" README, section
 // "FP8 W8A16 weight-only quantization", Analysis: the FP8->BF16 dequant GEMM spends
@@ -11,11 +12,14 @@
 //   W8A8 INT8: v_mfma_i32_16x16x64_i8 on the codes (exact int32)
 //   W8A8 FP8:  v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3) on the codes
 // The W8A8 epilogue takes a per-token scale per row when the call passes one.
-// M <= 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
+// 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
 //
-// Work split: workgroup (nt, s) owns output columns [16 nt, 16 nt + 16 CT) (CT
-// column tiles, see the kernel) and the s-th slice of K; its NW (4, 8 or 16) waves
-// take consecutive sub-slices.  The
+// Work split: workgroup (rg, nt, s) owns rows [16 rg, 16 rg + 16), output columns
+// [16 nt, 16 nt + 16 CT) (CT column tiles, see the kernel) and the s-th slice of K;
+// its NW (4, 8 or 16) waves take consecutive sub-slices.  With several row groups
+// (M > 16) the groups of one column tile and slice are consecutive in an XCD-grouped
+// order, so they run together on one XCD and all but the first read the weights from
+// its L2.  The
 // wave accumulators are summed through LDS; with S > 1 slices per column block the
 // partial sums go to the workspace and the last workgroup to arrive adds them
 // in slice order (deterministic) and runs the epilogue.  The handoff uses
@@ -83,7 +87,9 @@ __device__ __forceinline__ u32x4 load_x_codes16(const uint8_t* row, int k, int K
 // Four waves per SIMD (at most 128 registers per lane) let two 8-wave or four 4-wave
 // workgroups share a CU (16 waves hold a CU alone); FP8 W8A8 with one tile keeps the
 // registers its longer units take and runs three.
-template <int QT, int SCH, bool FAST, int NW, int CT = 1>
+// RG: several 16-row groups (M > 16; aligned path).  A separate build, so that the
+// single-group kernel keeps its code: the group arithmetic cost it 2-6 %.
+template <int QT, int SCH, bool FAST, int NW, int CT = 1, bool RG = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     (NW == 16 || (SCH == kW8A8 && QT == kFp8 && CT == 1)) ? 1 : 4))) void gemm_small_kernel(GemmArgs a, int S, int ups,
                                                                                           int upw) {
@@ -91,6 +97,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   constexpr int TPU = T::kTilesPerUnit;
   constexpr int kU = kUnroll / CT;                         // units per load batch
   static_assert(CT == 1 || ((CT == 2 || CT == 4) && FAST), "several column tiles on the aligned path only");
+  static_assert(!RG || FAST, "several row groups on the aligned path only");
   // The wave index is uniform across the wave: reading it once keeps the unit range and
   // the loop control in scalar registers.  Chosen per build: it pays with one tile
   // except for 16-wave INT8 W8A16 (K-sliced down projections ran 3 % slower; the FP8
@@ -100,8 +107,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = kScalarWave ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int NTG = (a.NT + CT - 1) / CT;                       // column-tile groups
-  const int nt = (blockIdx.x % NTG) * CT;                     // first column tile of the group
-  const int s = blockIdx.x / NTG;
+  const int NRG = RG ? (a.M + 15) >> 4 : 1;                   // 16-row groups
+  int rg = 0, nt, s;
+  if constexpr (RG) {
+    const int logical = xcd_remap(blockIdx.x, NTG * S * NRG);
+    rg = logical % NRG;
+    nt = (logical / NRG % NTG) * CT;
+    s = logical / NRG / NTG;
+  } else {
+    nt = (blockIdx.x % NTG) * CT;                             // first column tile of the group
+    s = blockIdx.x / NTG;
+  }
+  const int m0 = rg * 16;                                     // first row of the group
+  const int rows = RG ? (a.M - m0 < 16 ? a.M - m0 : 16) : a.M;
   const int KU = (a.KT + TPU - 1) / TPU;
   const int u_begin = s * ups + wave * upw;
   int u_end = u_begin + upw;
@@ -118,8 +136,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     sc_m128[c] = -128.0f * sc[c];
   }
 
-  // Row m = r of the A operand; rows >= M contribute zeros.
-  const bool row_ok = r < a.M;
+  // Row m0 + r of the A operand; rows >= M contribute zeros.
+  const bool row_ok = r < rows;
   const uint8_t* wbase = a.w + (int64_t)nt * a.KT * kTileBytes + lane * 16;
 
   f32x4 accf[CT];
@@ -152,8 +170,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     // wait for all of them.  The buffer range check returns zeros for activation
     // rows >= M and for the K tile past the end (odd tile count with two tiles per
     // unit); zero codes and zero activations add +0 to an accumulator that starts
-    // at +0, so the sums are unchanged.  Offsets stay below 2^31: M <= 16 and
-    // K <= 2^24 bound both buffers to 2^29 bytes.
+    // at +0, so the sums are unchanged.  Offsets stay below 2^31: 16 rows of the
+    // group and K <= 2^24 bound both buffers to 2^29 bytes.
     // The group's column tiles are consecutive in the packed weights; a tile past the
     // last one lies past the range and reads zeros.  With several column tiles the K
     // tile past the end of tile c would be the first K tile of tile c + 1, so that tile's
@@ -163,8 +181,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
         const_cast<uint8_t*>(a.w) + (int64_t)nt * a.KT * kTileBytes, 0, tiles_here * a.KT * kTileBytes,
         kBufferWord3);
     constexpr int kEsz = SCH == kW8A16 ? 2 : 1;
-    const __amdgpu_buffer_rsrc_t xrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), 0, a.M * a.K * kEsz, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.x)) + (int64_t)m0 * a.K * kEsz, 0,
+        rows * a.K * kEsz, kBufferWord3);
     const uint32_t xrow = row_ok ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
     auto run = [&](int u0, auto nu) {
       constexpr int NU = decltype(nu)::value;
@@ -236,11 +255,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           xb[i][t] = (u32x4){0u, 0u, 0u, 0u};
           if constexpr (SCH == kW8A16) {
             if (ok && row_ok)
-              load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)r * a.K, kt * kTileK + g * 16,
+              load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)(m0 + r) * a.K, kt * kTileK + g * 16,
                                    a.K, xa[i][t], xb[i][t]);
           } else {
             if (ok && row_ok)
-              xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)r * a.K,
+              xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)(m0 + r) * a.K,
                                               kt * kTileK + g * 16, a.K);
           }
         }
@@ -274,13 +293,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   // sums the slices in order
   if (CT == 1 && S > 1) {
     const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
-    store_partial(part, ((int64_t)s * a.NT + nt) * 64 + lane, tot);
+    // partial of (slice, row group, column tile); one counter per (row group, column tile)
+    const int64_t col = RG ? (int64_t)rg * a.NT + nt : nt;
+    const int64_t slice = RG ? (int64_t)NRG * a.NT : a.NT;
+    store_partial(part, ((int64_t)s * slice + col) * 64 + lane, tot);
     wait_stores_performed();
     // The fences pin the order at the compiler level too: partial stores before the
     // arrival, partial loads after it (at workgroup scope they add no cache maintenance).
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     uint32_t prev = 0;
-    if (lane == 0) prev = arrive(&a.counters[nt]);
+    if (lane == 0) prev = arrive(&a.counters[col]);
     prev = __shfl(prev, 0, 64);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (prev != (uint32_t)(S - 1)) return;
@@ -289,24 +311,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     if constexpr (T::kIntAcc) {
       i32x4 t = {0, 0, 0, 0};
       for (int q = 0; q < S; ++q)
-        t += __builtin_bit_cast(i32x4, q == s ? tot : load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane));
+        t += __builtin_bit_cast(i32x4, q == s ? tot : load_partial(part, ((int64_t)q * slice + col) * 64 + lane));
       tot = __builtin_bit_cast(f32x4, t);
     } else {
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < S; ++q) t += q == s ? tot : load_partial(part, ((int64_t)q * a.NT + nt) * 64 + lane);
+      for (int q = 0; q < S; ++q) t += q == s ? tot : load_partial(part, ((int64_t)q * slice + col) * 64 + lane);
       tot = t;
     }
-    if (lane == 0) reset_counter(&a.counters[nt]);
+    if (lane == 0) reset_counter(&a.counters[col]);
   }
 
-  // ---- epilogue: lane holds D[4g + j][r] = y[m = 4g + j, n]
+  // ---- epilogue: lane holds D[4g + j][r] = y[m = m0 + 4g + j, n]
   const int n = (nt + cw) * kTileN + r;
   if (n >= a.N) return;
   float sw = 0.0f;
   if (SCH == kW8A8 && !a.out_acc) sw = a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = 4 * g + j;
+    const int m = m0 + 4 * g + j;
     if (m >= a.M) break;
     const int64_t o = (int64_t)m * a.N + n;
     if constexpr (SCH == kW8A16) {
@@ -321,8 +343,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+template <int QT, int SCH, int NW, bool RG>
+hipError_t launch_small_rg(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  // several row groups: planned for the aligned path only
+  if (!a.fast) return hipErrorInvalidValue;
+  if (p.ct == 2)
+    gemm_small_kernel<QT, SCH, true, NW, 2, RG><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  else if (p.ct == 4)
+    gemm_small_kernel<QT, SCH, true, NW, 4, RG><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  else if (p.ct != 1)
+    return hipErrorInvalidValue;
+  else if constexpr (SCH == kW8A8 && QT == kFp8 && NW == 16)
+    return hipErrorInvalidValue;   // one FP8 W8A8 tile stops at 8 waves (16 would spill)
+  else
+    gemm_small_kernel<QT, SCH, true, NW, 1, RG><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  return hipGetLastError();
+}
+
 template <int QT, int SCH, int NW>
 hipError_t launch_small_w(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  if (a.M > 16) return launch_small_rg<QT, SCH, NW, true>(p, a, st);
   if (p.ct != 1) {
     // several column tiles per workgroup: planned for the aligned path without K slices only
     if (!a.fast || p.S != 1) return hipErrorInvalidValue;

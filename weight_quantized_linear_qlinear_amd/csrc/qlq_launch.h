@@ -12,7 +12,7 @@ enum Scheme : int { kW8A16 = 0, kW8A8 = 1 };
 
 // How one GEMM call is cut into workgroups.
 struct GemmPlan {
-  int kind = 0;             // 0: small-M family (M <= 16), 1: large-M register-staged
+  int kind = 0;             // 0: small-M family (16-row groups), 1: large-M register-staged
                             // (any K), 2: large-M direct-to-LDS (K % 64 == 0)
   int cfg = 0;              // kind 2: tile configuration (see gemm_mfma.hip)
   int S = 1;                // split-K factor (workgroups sharing one output tile)
