@@ -313,7 +313,7 @@ def kv_rows(qlq, torch, dev, Ts, steps, warmup):
     return res
 
 
-BUCKET_M = (1, 5, 13, 100, 300)     # batch sizes that are not buckets (except 1), padded to 1, 8, 16, 128, 512
+BUCKET_M = (1, 5, 13, 30, 50, 100, 300)   # not buckets (except 1): padded to 1, 8, 16, 32, 64, 128, 512
 
 
 def bucket_rows(qlq, synth, torch, dev, qi, L, steps, warmup):
