@@ -17,12 +17,12 @@ from tests.gpu_util import bf16_bits, bf16_to_gpu, bits_to_f64, check_close, cod
 pytestmark = pytest.mark.gpu
 
 QTYPES = ["int8", "fp8_e4m3fn"]
-# small-M kernel (with one and with several 16-column tiles per workgroup), direct-to-LDS
-# kernel (K % 64 == 0), register-staged kernel (ragged K), split-K plans, tails in every
-# dimension
+# small-M kernel (with one and with several 16-column tiles per workgroup, and several 16-row
+# groups with and without K slices), direct-to-LDS kernel (K % 64 == 0), register-staged kernel
+# (ragged K), split-K plans, tails in every dimension
 SHAPES = [(1, 1, 1), (1, 64, 16), (2, 5, 3), (1, 2048, 2048), (3, 100, 37), (16, 640, 200), (13, 1000, 300),
           (16, 11008, 128), (17, 640, 200), (31, 512, 129), (64, 128, 4096), (255, 1024, 136), (257, 320, 250),
-          (130, 4096, 96), (37, 1000, 300), (300, 100, 1100), (13, 704, 10338)]
+          (130, 4096, 96), (37, 1000, 300), (300, 100, 1100), (13, 704, 10338), (20, 8192, 1024)]
 
 
 def _rows_spread(x_bits, seed):

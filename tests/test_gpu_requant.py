@@ -24,11 +24,11 @@ from tests.gpu_util import bf16_bits, bf16_to_gpu, bits_to_f64, check_close, cod
 pytestmark = pytest.mark.gpu
 
 QTYPES = ["int8", "fp8_e4m3fn"]
-# small-M kernel (4/8/16 waves, split-K, unaligned N), direct-to-LDS kernel (staged and
-# direct epilogues, split-K), register-staged kernel (K not a multiple of 64, with and without
-# split-K)
+# small-M kernel (4/8/16 waves, split-K, unaligned N, several 16-row groups with and without
+# split-K), direct-to-LDS kernel (staged and direct epilogues, split-K), register-staged kernel
+# (K not a multiple of 64, with and without split-K)
 SHAPES = [(1, 1, 1), (1, 2048, 1024), (1, 2048, 2048), (3, 100, 37), (16, 640, 200), (16, 11008, 128),
-          (64, 128, 4096), (130, 4096, 96), (255, 1024, 136), (257, 320, 250), (256, 11008, 256),
+          (64, 128, 4096), (20, 8192, 1024), (130, 4096, 96), (255, 1024, 136), (257, 320, 250), (256, 11008, 256),
           (1024, 2048, 1024), (130, 1000, 96), (40, 200, 64), (300, 2000, 300),
           # plans of the 3B-scale stack's chain: small-M without split (4 waves) and with split
           # (8 / 16 waves), two 16-column tiles per workgroup (up projection at M = 16), and
