@@ -412,9 +412,9 @@ def test_small_m_column_tile_plans_keep_their_invariants():
 
 def test_batched_decode_plans_take_row_groups():
     """From 17 to 64 rows on aligned K, the small-M kernel runs one workgroup per 16-row
-    group when it measured faster than the direct-to-LDS kernel: two groups unless K is
-    12288 or more, three or four only for weights of at most 8M codes; ragged K and larger
-    M keep the large-M kernels.  The grid and workspace count every group, and K slices
+    group when it measured faster than the direct-to-LDS kernel: always for outputs of
+    fewer than 128 column tiles; otherwise two groups below K = 12288, three for weights of
+    at most 20M codes, four for at most 12M; ragged K and larger M keep the large-M kernels.  The grid and workspace count every group, and K slices
     keep one arrival counter per (group, column tile) inside the counter region."""
     def cdiv(a, b):
         return -(-a // b)
@@ -423,12 +423,13 @@ def test_batched_decode_plans_take_row_groups():
         for qt in ("int8", "fp8_e4m3fn"):
             for M in (16, 17, 24, 32, 33, 48, 64, 65, 100):
                 for K in (64, 1000, 2048, 4096, 11008, 12288, 14336):
-                    for N in (16, 1024, 2048, 4096, 11008):
+                    for N in (16, 1024, 2048, 4096, 5632, 11008):
                         p = qlq.gemm_plan(sch, M, K, N, qt)
                         where = (sch, qt, M, K, N, p)
                         nrg = cdiv(M, 16)
+                        limit = {3: 20 << 20, 4: 12 << 20}.get(nrg, 0)
                         small = M <= 16 or (M <= 64 and K % 64 == 0 and
-                                            (K < 12288 if nrg <= 2 else N * K <= 8 << 20))
+                                            (cdiv(N, 16) < 128 or (K < 12288 if nrg <= 2 else N * K <= limit)))
                         assert (p["kind"] == 0) == small, where
                         if p["kind"] != 0:
                             continue

@@ -170,14 +170,21 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
   // Batched decode (16 < M <= 64, aligned path): the small-M kernel with one workgroup
   // per 16-row group (each group re-reads the weights, from L2 when its siblings run
   // beside it) against the direct-to-LDS kernel, whose 128-row tiles stream 128 rows
-  // of x whatever M is.  Same-box timings (INT8 W8A16, FP8 and INT8 W8A8, stack and
-  // 7-8B shapes): with two groups (M <= 32) the small-M kernel took 0.36-0.85 of the
-  // time (2048 -> 2048: 13.4 -> 4.8 us; 11008 -> 2048: 23.7 -> 19.5) except on deep
-  // weights (14336 -> 4096: 1.11); with three or four only small weights gained
-  // (2048 x 2048 and 4096 -> 1024: 0.4-0.6; 4096 x 4096 1.10, 11008 -> 2048 up to 1.5).
+  // of x whatever M is.  Same-box timings (INT8 W8A16 and FP8 W8A8 over 17 shapes from
+  // 1024 to 28672 inputs and outputs; INT8 W8A8 on the stack's): narrow outputs (fewer
+  // than 128 column tiles) ran faster with the groups at every M (14336 -> 1024 at M =
+  // 24: 25.0 -> 12.4 us); with two groups wider outputs did too (0.36-0.85 of the time)
+  // except over K >= 12288 (14336 -> 4096: 1.11, 13824 -> 5120: 1.23-1.28); with three
+  // groups weights up to about 17M codes gained (0.78-0.95; 22.5M mixed, 0.85-1.17;
+  // larger slower) and with four only up to about 12M (2048 -> 5632: 0.79-0.82; 16.8M
+  // 0.91-1.10; larger up to 1.8).
   bool small = M <= 16;
-  if (!small && aligned_path && M <= kSmallMaxRows)
-    small = cdiv(M, 16) <= 2 ? K < 12288 : N * K <= (int64_t(8) << 20);
+  if (!small && aligned_path && M <= kSmallMaxRows) {
+    const int64_t groups = cdiv(M, 16), NT = cdiv(N, 16);
+    if (NT < 128) small = true;
+    else if (groups <= 2) small = K < 12288;
+    else small = N * K <= (groups == 3 ? int64_t(20) << 20 : int64_t(12) << 20);
+  }
   if (!small && aligned_path) return plan_mfma(scheme, M, K, N);
   GemmPlan p;
   const int64_t KT = cdiv(K, 64), NT = cdiv(N, 16);
