@@ -292,7 +292,7 @@ qlq_status qlq_kv_dequantize(const void* k_codes, const void* k_scales, const vo
 
 /* The launch plan a GEMM call takes for these sizes when x is 16-byte aligned (what
  * the tests use to show which kernel configuration a case reaches).  kind 0 is the
- * small-M family (M <= 16, or up to 64 rows with K a multiple of 64; tile_m = 16
+ * small-M family (M <= 16, or up to 128 rows with K a multiple of 64; tile_m = 16
  * rows per workgroup, tile_n = 16, 32 or 64 columns per workgroup, `waves` waves per
  * workgroup), 1 the register-staged large-M kernel
  * (K not a multiple of 64), 2 the direct-to-LDS large-M kernel with tile

@@ -415,14 +415,15 @@ def test_batched_decode_plans_take_row_groups():
     group when it measured faster than the direct-to-LDS kernel: always for outputs of
     fewer than 128 column tiles; otherwise two groups below K = 12288, three for weights of
     at most 20M codes (W8A16 over K <= 8192: 28M), four for at most 12M (W8A16 over K = 2048:
-    24M); ragged K and larger M keep the large-M kernels.  The grid and workspace count every group, and K slices
+    24M); from 65 to 128 rows only narrow outputs over K <= 4096; ragged K and larger M keep
+    the large-M kernels.  The grid and workspace count every group, and K slices
     keep one arrival counter per (group, column tile) inside the counter region."""
     def cdiv(a, b):
         return -(-a // b)
 
     for sch in ("w8a16", "w8a8_static"):
         for qt in ("int8", "fp8_e4m3fn"):
-            for M in (16, 17, 24, 32, 33, 48, 64, 65, 100):
+            for M in (16, 17, 24, 32, 33, 48, 64, 65, 100, 128, 129):
                 for K in (64, 1000, 2048, 3072, 4096, 8192, 11008, 12288, 14336):
                     for N in (16, 1024, 2048, 4096, 5632, 8192, 11008):
                         p = qlq.gemm_plan(sch, M, K, N, qt)
@@ -431,8 +432,15 @@ def test_batched_decode_plans_take_row_groups():
                         w16 = sch == "w8a16"
                         by_size = {3: N * K <= (28 << 20 if w16 and K <= 8192 else 20 << 20),
                                    4: N * K <= 12 << 20 or (w16 and K <= 2048 and N * K <= 24 << 20)}
-                        small = M <= 16 or (M <= 64 and K % 64 == 0 and
-                                            (cdiv(N, 16) < 128 or (K < 12288 if nrg <= 2 else by_size[nrg])))
+                        narrow = cdiv(N, 16) < 128
+                        if M <= 16:
+                            small = True
+                        elif K % 64 or M > 128:
+                            small = False
+                        elif nrg > 4:
+                            small = narrow and K <= 4096
+                        else:
+                            small = narrow or (K < 12288 if nrg <= 2 else by_size[nrg])
                         assert (p["kind"] == 0) == small, where
                         if p["kind"] != 0:
                             continue

@@ -35,7 +35,8 @@ W8A8_PLAN_SHAPES = [(769, 1024, 14026),   # 256x256 eight waves, no split
                     (513, 6976, 13393),   # 256x256 three-stage ring, no split
                     (535, 512, 13175),    # 256x192, no split
                     (129, 9472, 11072),   # 256x192, K slices
-                    (65, 960, 16)]        # 128x128 four waves, K slices
+                    (161, 960, 100),      # 128x128 four waves, K slices
+                    (161, 64, 100)]       # 128x128 four waves of 64x64, no split
 
 
 # (M, K, N) -> small-M plans (waves per workgroup, column tiles per workgroup, K slices,
@@ -63,7 +64,8 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (17, 2112, 16), (17, 4160, 16), (17, 8576, 1014),     # K slices, one column
                      (17, 64, 5127), (17, 64, 10611), (17, 512, 5127),     # two and four column tiles
                      (17, 960, 10611), (17, 960, 5127), (33, 4160, 1604),  # up to 16 waves, three groups
-                     (17, 4544, 1014), (17, 4096, 2385), (20, 6464, 16)]    # K slices, 4 / 8 waves
+                     (17, 4544, 1014), (17, 4096, 2385), (20, 6464, 16),    # K slices, 4 / 8 waves
+                     (100, 1024, 500), (128, 4096, 100)]                    # narrow: 7 and 8 groups
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

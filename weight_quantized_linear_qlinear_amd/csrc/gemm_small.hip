@@ -1,4 +1,4 @@
-// Small-M (decode, M <= 16; batched decode up to 64 rows in 16-row groups) quantized
+// Small-M (decode, M <= 16; batched decode up to 128 rows in 16-row groups) quantized
 // GEMM family.
 //
 // Decode is bound by reading the weights once ("Nano-vLLM-MoE" README, section
