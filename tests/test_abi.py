@@ -415,8 +415,8 @@ def test_batched_decode_plans_take_row_groups():
     group when it measured faster than the direct-to-LDS kernel: always for outputs of
     fewer than 128 column tiles; otherwise two groups below K = 12288, three for weights of
     at most 20M codes (W8A16 over K <= 8192: 28M), four for at most 12M (W8A16 over K = 2048:
-    24M); from 65 to 128 rows only narrow outputs over K <= 4096; ragged K and larger M keep
-    the large-M kernels.  The grid and workspace count every group, and K slices
+    24M); from 65 to 128 rows narrow outputs over K <= 4096 and weights of at most 4M codes
+    on at most 128 column tiles; ragged K and larger M keep the large-M kernels.  The grid and workspace count every group, and K slices
     keep one arrival counter per (group, column tile) inside the counter region."""
     def cdiv(a, b):
         return -(-a // b)
@@ -438,7 +438,7 @@ def test_batched_decode_plans_take_row_groups():
                         elif K % 64 or M > 128:
                             small = False
                         elif nrg > 4:
-                            small = narrow and K <= 4096
+                            small = (narrow and K <= 4096) or (cdiv(N, 16) <= 128 and N * K <= 4 << 20)
                         else:
                             small = narrow or (K < 12288 if nrg <= 2 else by_size[nrg])
                         assert (p["kind"] == 0) == small, where

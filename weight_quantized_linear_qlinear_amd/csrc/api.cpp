@@ -46,7 +46,7 @@ constexpr int64_t kMaxSplitTiles = 1024;
 constexpr size_t kCounterBytes = kMaxSplitTiles * 4;
 constexpr int64_t kSmallUnitsPerWave = 8;   // matches kUnroll of the small-M kernel
 // Batched decode: the small-M kernel takes up to this many rows (16-row groups, aligned
-// path; above 64 rows narrow, shallow weights only) before the direct-to-LDS kernel's
+// path; above 64 rows narrow or small weights only) before the direct-to-LDS kernel's
 // 128-row tiles (see plan_gemm).  Eight groups of at most 127 column tiles keep one split-K
 // arrival counter per (group, column tile) inside the counter region.
 constexpr int64_t kSmallMaxRows = 128;
@@ -180,12 +180,14 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
   // groups weights up to about 17M codes gained (0.78-0.95; 22.5M mixed, 0.85-1.17;
   // larger slower; W8A16 up to 26M over K <= 8192: 0.78-0.89) and with four only up to
   // about 12M (2048 -> 5632: 0.79-0.82; 16.8M 0.91-1.10; larger up to 1.8; W8A16 over
-  // K = 2048 up to 22.5M: 0.79-0.91).  From 65 to 128 rows only narrow outputs over
-  // K <= 4096 gained (0.44-0.72; K = 8192 0.93-1.02, deeper up to 1.9).
+  // K = 2048 up to 22.5M: 0.79-0.91).  From 65 to 128 rows narrow outputs over K <= 4096
+  // gained (0.44-0.72; K = 8192 0.93-1.02, deeper up to 1.9), and of wider ones only
+  // weights of at most 4M codes on at most 128 column tiles (2048 x 2048: 0.69-0.83;
+  // 1024 -> 4096 0.74-1.30, 2048 -> 4096 0.96-1.35, larger up to 1.9).
   bool small = M <= 16;
   if (!small && aligned_path && M <= kSmallMaxRows) {
     const int64_t groups = cdiv(M, 16), NT = cdiv(N, 16);
-    if (groups > 4) small = NT < 128 && K <= 4096;
+    if (groups > 4) small = (NT < 128 && K <= 4096) || (NT <= 128 && N * K <= (int64_t(4) << 20));
     else if (NT < 128) small = true;
     else if (groups <= 2) small = K < 12288;
     else if (groups == 3) small = N * K <= ((scheme == kW8A16 && K <= 8192 ? int64_t(28) : int64_t(20)) << 20);
