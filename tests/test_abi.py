@@ -414,7 +414,8 @@ def test_batched_decode_plans_take_row_groups():
     """From 17 to 64 rows on aligned K, the small-M kernel runs one workgroup per 16-row
     group when it measured faster than the direct-to-LDS kernel: always for outputs of
     fewer than 128 column tiles; otherwise two groups below K = 12288, three for weights of
-    at most 20M codes (W8A16 over K <= 8192: 28M), four for at most 12M (W8A16 over K = 2048:
+    at most 20M codes (over K <= 8192: 28M, for W8A8 on at most 512 column tiles), four for
+    at most 12M (W8A16 over K = 2048:
     24M); from 65 to 128 rows narrow outputs over K <= 4096 and weights of at most 4M codes
     on at most 128 column tiles; ragged K and larger M keep the large-M kernels.  The grid and workspace count every group, and K slices
     keep one arrival counter per (group, column tile) inside the counter region."""
@@ -430,7 +431,8 @@ def test_batched_decode_plans_take_row_groups():
                         where = (sch, qt, M, K, N, p)
                         nrg = cdiv(M, 16)
                         w16 = sch == "w8a16"
-                        by_size = {3: N * K <= (28 << 20 if w16 and K <= 8192 else 20 << 20),
+                        by_size = {3: N * K <= 20 << 20 or (K <= 8192 and N * K <= 28 << 20 and
+                                                              (w16 or cdiv(N, 16) <= 512)),
                                    4: N * K <= 12 << 20 or (w16 and K <= 2048 and N * K <= 24 << 20)}
                         narrow = cdiv(N, 16) < 128
                         if M <= 16:

@@ -178,7 +178,8 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
   // 24: 25.0 -> 12.4 us); with two groups wider outputs did too (0.36-0.85 of the time)
   // except over K >= 12288 (14336 -> 4096: 1.11, 13824 -> 5120: 1.23-1.28); with three
   // groups weights up to about 17M codes gained (0.78-0.95; 22.5M mixed, 0.85-1.17;
-  // larger slower; W8A16 up to 26M over K <= 8192: 0.78-0.89) and with four only up to
+  // larger slower; up to 26M over K <= 8192: W8A16 0.78-0.89, W8A8 on at most 512 column
+  // tiles 0.86-0.88 (3072 -> 8192 and 5120 x 5120), on 688 1.0-1.14) and with four only up to
   // about 12M (2048 -> 5632: 0.79-0.82; 16.8M 0.91-1.10; larger up to 1.8; W8A16 over
   // K = 2048 up to 22.5M: 0.79-0.91).  From 65 to 128 rows narrow outputs over K <= 4096
   // gained (0.44-0.72; K = 8192 0.93-1.02, deeper up to 1.9), and of wider ones only
@@ -190,7 +191,9 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     if (groups > 4) small = (NT < 128 && K <= 4096) || (NT <= 128 && N * K <= (int64_t(4) << 20));
     else if (NT < 128) small = true;
     else if (groups <= 2) small = K < 12288;
-    else if (groups == 3) small = N * K <= ((scheme == kW8A16 && K <= 8192 ? int64_t(28) : int64_t(20)) << 20);
+    else if (groups == 3)
+      small = N * K <= (int64_t(20) << 20) ||
+              (K <= 8192 && N * K <= (int64_t(28) << 20) && (scheme == kW8A16 || NT <= 512));
     else small = N * K <= (int64_t(12) << 20) || (scheme == kW8A16 && K <= 2048 && N * K <= (int64_t(24) << 20));
   }
   if (!small && aligned_path) return plan_mfma(scheme, M, K, N);
