@@ -349,7 +349,7 @@ def test_parity_shapes_reach_every_launch_plan():
 
     def key(mkn, p):
         if p["kind"] == 0:
-            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0, p["tile_n"], mkn[0] > 16
+            return 0, p["waves"], p["split_k"] > 1, mkn[1] % 64 == 0, p["tile_n"], mkn[0] > 16, p["tile_m"]
         return p["kind"], p["cfg"], p["split_k"] > 1
 
     grid = [(M, K, N) for M in range(17, 1100, 48) for K in range(64, 11100, 64 * 7)
@@ -411,14 +411,16 @@ def test_small_m_column_tile_plans_keep_their_invariants():
 
 
 def test_batched_decode_plans_take_row_groups():
-    """From 17 to 64 rows on aligned K, the small-M kernel runs one workgroup per 16-row
-    group when it measured faster than the direct-to-LDS kernel: always for outputs of
-    fewer than 128 column tiles; otherwise two groups below K = 12288, three for weights of
-    at most 20M codes (over K <= 8192: 28M, for W8A8 on at most 512 column tiles), four for
-    at most 12M (W8A16 over K = 2048:
-    24M); from 65 to 128 rows narrow outputs over K <= 4096 and weights of at most 4M codes
-    on at most 128 column tiles; ragged K and larger M keep the large-M kernels.  The grid and workspace count every group, and K slices
-    keep one arrival counter per (group, column tile) inside the counter region."""
+    """From 17 to 128 rows on aligned K, the small-M kernel runs one workgroup per 16-row
+    group when it measured faster than the direct-to-LDS kernel: up to 64 rows always for
+    outputs of fewer than 128 column tiles, otherwise two groups below K = 12288, three for
+    weights of at most 20M codes (over K <= 8192: 28M, for W8A8 on at most 512 column
+    tiles), four for at most 12M (W8A16 over K = 2048: 24M); from 65 to 128 rows narrow
+    outputs over K <= 4096 and weights of at most 4M codes on at most 128 column tiles;
+    ragged K and larger M keep the large-M kernels.  Two groups share a workgroup (tile_m
+    32) on weights of at least 128 column tiles over K >= 8192 with one column tile per
+    workgroup.  The grid and workspace count every group, and K slices keep one arrival
+    counter per (group, column tile) inside the counter region."""
     def cdiv(a, b):
         return -(-a // b)
 
@@ -446,8 +448,12 @@ def test_batched_decode_plans_take_row_groups():
                         assert (p["kind"] == 0) == small, where
                         if p["kind"] != 0:
                             continue
-                        NT, ct, S = cdiv(N, 16), p["tile_n"] // 16, p["split_k"]
-                        assert p["tile_m"] == 16 and p["grid"] == cdiv(NT, ct) * S * nrg, where
+                        NT, ct, S, rw = cdiv(N, 16), p["tile_n"] // 16, p["split_k"], p["tile_m"] // 16
+                        pair = nrg == 2 and ct == 1 and K >= 8192 and NT >= 128
+                        if sch != "w8a16" and qt == "fp8_e4m3fn" and p["waves"] == 16:
+                            pair = False                  # no 16-wave FP8 W8A8 pair build
+                        assert rw == (2 if pair else 1), where
+                        assert p["grid"] == cdiv(NT, ct) * S * cdiv(nrg, rw), where
                         if S > 1:
                             assert NT * nrg <= 1024 and p["workspace_bytes"] >= S * nrg * NT * 1024, where
 

@@ -66,7 +66,9 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (17, 960, 10611), (17, 960, 5127), (33, 4160, 1604),  # up to 16 waves, three groups
                      (17, 4544, 1014), (17, 4096, 2385), (20, 6464, 16),    # K slices, 4 / 8 waves
                      (100, 1024, 500), (128, 4096, 100),                    # narrow: 7 and 8 groups
-                     (80, 1024, 2048)]                                      # 128 column tiles, 5 groups
+                     (80, 1024, 2048),                                      # 128 column tiles, 5 groups
+                     # two row groups per workgroup (deep weights): K slices or not, 4 to 16 waves
+                     (17, 8576, 2385), (17, 8576, 3299), (17, 8576, 4213)]
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

@@ -304,6 +304,14 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
       // faster than eight in the third sweep.
       if (ct == 1 && S == 1 && TPU == 2 && NT >= 256 && KU >= 64) W = 4;
     }
+    // Two row groups per workgroup (each unit's weights loaded once for both) on deep
+    // weights with one column tile: same-box timings at M = 17 / 24 / 32 over 8192 and
+    // 11008 inputs to 2048 and 4096 outputs, all three schemes, 0.61-0.83 / 0.69-0.92 /
+    // 0.78-0.99 of the time with one group per workgroup (11008 -> 4096 INT8 W8A16 at
+    // M = 17: 26.7 -> 16.7 us); on shallower or narrower weights the halved grid lost
+    // (2048 x 2048 at M = 24: 1.12-1.19x; 14336 -> 1024: 1.18-1.25x).
+    int64_t rw = 1;
+    if (NRG == 2 && ct == 1 && fast && K >= 8192 && NT >= 128 && !(TPU == 2 && W == 16)) rw = 2;   // no 16-wave FP8 W8A8 pair build
     // One arrival counter per (row group, column tile): NRG <= 4 keeps every split plan
     // above (fewer than 192 column tiles, or one row group) within the counter region.
     if (S > 1 && NT * NRG > kMaxSplitTiles) {
@@ -312,11 +320,12 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     }
     p.S = (int)S;
     p.ct = (int)ct;
+    p.rw = (int)rw;
     p.units_per_split = (int)ups;
     p.units_per_wave = (int)cdiv(ups, W);
     p.waves = (int)W;
     p.tiles = (int)NT;
-    p.grid = (int)(cdiv(NT, ct) * S * NRG);
+    p.grid = (int)(cdiv(NT, ct) * S * cdiv(NRG, rw));
     if (S > 1) {   // S > 1 only when NT < 192 or 256 < NT <= kMaxSplitTiles
       p.ws_counter_bytes = kCounterBytes;
       p.ws_bytes = p.ws_counter_bytes + (size_t)S * NRG * NT * 64 * 16;
@@ -748,7 +757,7 @@ qlq_status qlq_gemm_plan(qlq_scheme scheme, int64_t M, int64_t K, int64_t N, qlq
   info->kind = p.kind;
   info->cfg = p.kind == 2 ? p.cfg : -1;
   info->split_k = p.S;
-  info->tile_m = p.kind == 0 ? 16 : p.BM;
+  info->tile_m = p.kind == 0 ? 16 * p.rw : p.BM;
   info->tile_n = p.kind == 0 ? 16 * p.ct : p.BN;
   info->waves = p.kind == 0 ? p.waves : 0;
   info->grid = p.grid;

@@ -14,12 +14,12 @@
 // The W8A8 epilogue takes a per-token scale per row when the call passes one.
 // 16 rows fill the MFMA's 16-row A operand (rows >= M are zero).
 //
-// Work split: workgroup (rg, nt, s) owns rows [16 rg, 16 rg + 16), output columns
-// [16 nt, 16 nt + 16 CT) (CT column tiles, see the kernel) and the s-th slice of K;
-// its NW (4, 8 or 16) waves take consecutive sub-slices.  With several row groups
-// (M > 16) the groups of one column tile and slice are consecutive in an XCD-grouped
-// order, so they run together on one XCD and all but the first read the weights from
-// its L2.  The
+// Work split: workgroup (rg, nt, s) owns rows [16 rg, 16 rg + 16 RW) (RW row groups),
+// output columns [16 nt, 16 nt + 16 CT) (CT column tiles, see the kernel) and the s-th
+// slice of K; its NW (4, 8 or 16) waves take consecutive sub-slices.  With several row
+// groups (M > 16) the workgroups of one column tile and slice are consecutive in an
+// XCD-grouped order, so they run together on one XCD and all but the first read the
+// weights from its L2.  The
 // wave accumulators are summed through LDS; with S > 1 slices per column block the
 // partial sums go to the workspace and the last workgroup to arrive adds them
 // in slice order (deterministic) and runs the epilogue.  The handoff uses
@@ -89,13 +89,17 @@ __device__ __forceinline__ u32x4 load_x_codes16(const uint8_t* row, int k, int K
 // registers its longer units take and runs three.
 // RG: several 16-row groups (M > 16; aligned path).  A separate build, so that the
 // single-group kernel keeps its code: the group arithmetic cost it 2-6 %.
-template <int QT, int SCH, bool FAST, int NW, int CT = 1, bool RG = false>
+// RW: row groups per workgroup (1 or 2; 2 with one column tile).  Each unit's weights
+// then serve both groups (one load, two MFMAs), and a load batch holds 8 / (CT RW) units
+// so the registers in flight stay those of eight single-group units.
+template <int QT, int SCH, bool FAST, int NW, int CT = 1, bool RG = false, int RW = 1>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     (NW == 16 || (SCH == kW8A8 && QT == kFp8 && CT == 1)) ? 1 : 4))) void gemm_small_kernel(GemmArgs a, int S, int ups,
                                                                                           int upw) {
   using T = SmallTraits<QT, SCH>;
   constexpr int TPU = T::kTilesPerUnit;
-  constexpr int kU = kUnroll / CT;                         // units per load batch
+  constexpr int kU = kUnroll / (CT * RW);                  // units per load batch
+  static_assert(RW == 1 || (RG && CT == 1), "row-group pairs: one column tile");
   static_assert(CT == 1 || ((CT == 2 || CT == 4) && FAST), "several column tiles on the aligned path only");
   static_assert(!RG || FAST, "several row groups on the aligned path only");
   // The wave index is uniform across the wave: reading it once keeps the unit range and
@@ -108,18 +112,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   const int wave = kScalarWave ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int NTG = (a.NT + CT - 1) / CT;                       // column-tile groups
   const int NRG = RG ? (a.M + 15) >> 4 : 1;                   // 16-row groups
+  const int NRP = (NRG + RW - 1) / RW;                        // groups of RW row groups
   int rg = 0, nt, s;
   if constexpr (RG) {
-    const int logical = xcd_remap(blockIdx.x, NTG * S * NRG);
-    rg = logical % NRG;
-    nt = (logical / NRG % NTG) * CT;
-    s = logical / NRG / NTG;
+    const int logical = xcd_remap(blockIdx.x, NTG * S * NRP);
+    rg = logical % NRP * RW;
+    nt = (logical / NRP % NTG) * CT;
+    s = logical / NRP / NTG;
   } else {
     nt = (blockIdx.x % NTG) * CT;                             // first column tile of the group
     s = blockIdx.x / NTG;
   }
   const int m0 = rg * 16;                                     // first row of the group
   const int rows = RG ? (a.M - m0 < 16 ? a.M - m0 : 16) : a.M;
+  // Rows of the second group of a pair (0 when the pair's first group is the last one).
+  // Uniform; the clamp compiles to a vector instruction, so it is read back into a
+  // scalar register for the buffer descriptor built from it.
+  const int left1 = a.M - m0 - 16;
+  const int rows1 = RW == 2 ? __builtin_amdgcn_readfirstlane(left1 < 0 ? 0 : (left1 < 16 ? left1 : 16)) : 0;
   const int KU = (a.KT + TPU - 1) / TPU;
   const int u_begin = s * ups + wave * upw;
   int u_end = u_begin + upw;
@@ -140,25 +150,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   const bool row_ok = r < rows;
   const uint8_t* wbase = a.w + (int64_t)nt * a.KT * kTileBytes + lane * 16;
 
-  f32x4 accf[CT];
-  i32x4 acci[CT];
+  f32x4 accf[RW][CT];
+  i32x4 acci[RW][CT];
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    accf[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    acci[c] = (i32x4){0, 0, 0, 0};
-  }
+  for (int q = 0; q < RW; ++q)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      accf[q][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      acci[q][c] = (i32x4){0, 0, 0, 0};
+    }
 
   // A unit's arithmetic for column tile c: dequantize (W8A16) and feed the MFMA.
-  auto unit_mma = [&](int c, const u32x4 (&wv)[TPU], const u32x4 (&xa)[TPU], const u32x4 (&xb)[TPU]) {
+  auto unit_mma = [&](int c, const u32x4 (&wv)[TPU], const u32x4 (&xa)[RW][TPU], const u32x4 (&xb)[RW][TPU]) {
     if constexpr (SCH == kW8A16) {
       bf16x8 b0 = dequant8<QT>(wv[0].x, wv[0].y, sc[c], sc_m128[c]);
       bf16x8 b1 = dequant8<QT>(wv[0].z, wv[0].w, sc[c], sc_m128[c]);
-      accf[c] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[0]), b0, accf[c]);
-      accf[c] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[0]), b1, accf[c]);
+#pragma unroll
+      for (int q = 0; q < RW; ++q) {
+        accf[q][c] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xa[q][0]), b0, accf[q][c]);
+        accf[q][c] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, xb[q][0]), b1, accf[q][c]);
+      }
     } else if constexpr (QT == kInt8) {
-      acci[c] = mfma_i8_k64(xa[0], wv[0], acci[c]);
+#pragma unroll
+      for (int q = 0; q < RW; ++q) acci[q][c] = mfma_i8_k64(xa[q][0], wv[0], acci[q][c]);
     } else {
-      accf[c] = mfma_fp8_k128(xa[0], xa[TPU - 1], wv[0], wv[TPU - 1], accf[c]);
+#pragma unroll
+      for (int q = 0; q < RW; ++q) accf[q][c] = mfma_fp8_k128(xa[q][0], xa[q][TPU - 1], wv[0], wv[TPU - 1], accf[q][c]);
     }
   };
 
@@ -185,9 +202,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
         const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.x)) + (int64_t)m0 * a.K * kEsz, 0,
         rows * a.K * kEsz, kBufferWord3);
     const uint32_t xrow = row_ok ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
+    // Second group of a pair: named values rather than arrays, which the compiler
+    // keeps in vector registers (every load then loops over the lanes' descriptors).
+    // A group past the last row has an empty range: its loads return zeros.
+    const __amdgpu_buffer_rsrc_t xrs1 = RW == 1 ? xrs : __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.x)) + (int64_t)(m0 + 16) * a.K * kEsz, 0,
+        rows1 * a.K * kEsz, kBufferWord3);
+    const uint32_t xrow1 = r < rows1 ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
     auto run = [&](int u0, auto nu) {
       constexpr int NU = decltype(nu)::value;
-      u32x4 wv[NU][CT][TPU], xa[NU][TPU], xb[NU][TPU];
+      u32x4 wv[NU][CT][TPU], xa[NU][RW][TPU], xb[NU][RW][TPU];
 #pragma unroll
       for (int i = 0; i < NU; ++i) {
 #pragma unroll
@@ -199,9 +223,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           for (int c = 0; c < CT; ++c)
             wv[i][c][t] = __builtin_amdgcn_raw_buffer_load_b128(
                 wrs, kt_in ? (c * a.KT + kt) * kTileBytes + lane * 16 : (int)0x80000000u, 0, kCachePolicyNt);
-          xa[i][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0);
-          xb[i][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(xo + 16), 0, 0)
-                                   : (u32x4){0u, 0u, 0u, 0u};
+          xa[i][0][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0);
+          xb[i][0][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(xo + 16), 0, 0)
+                                      : (u32x4){0u, 0u, 0u, 0u};
+          if constexpr (RW == 2) {
+            const uint32_t xo1 = kt_in ? xrow1 + (uint32_t)(kt * kTileK * kEsz) : 0x80000000u;
+            xa[i][1][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs1, (int)xo1, 0, 0);
+            xb[i][1][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs1, (int)(xo1 + 16), 0, 0)
+                                        : (u32x4){0u, 0u, 0u, 0u};
+          }
         }
         __builtin_amdgcn_sched_barrier(0);   // issue order = unit order
       }
@@ -241,8 +271,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     // Generic path: per-element bounds checks.
     for (int u0 = u_begin; u0 < u_end; u0 += kU) {
       u32x4 wv[kU][TPU];
-      u32x4 xa[kU][TPU];      // A operand bytes: 16 codes, or 8 bf16 (W8A16: values 0..7)
-      u32x4 xb[kU][TPU];      // W8A16: bf16 values 8 .. 15
+      u32x4 xa[kU][RW][TPU];  // A operand bytes: 16 codes, or 8 bf16 (W8A16: values 0..7)
+      u32x4 xb[kU][RW][TPU];  // W8A16: bf16 values 8 .. 15
 #pragma unroll
       for (int i = 0; i < kU; ++i) {
         const bool live = u0 + i < u_end;
@@ -251,16 +281,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           const int kt = (u0 + i) * TPU + t;
           const bool ok = live && kt < a.KT;
           wv[i][t] = ok ? ld16_stream(wbase + (int64_t)kt * kTileBytes) : (u32x4){0u, 0u, 0u, 0u};
-          xa[i][t] = (u32x4){0u, 0u, 0u, 0u};
-          xb[i][t] = (u32x4){0u, 0u, 0u, 0u};
+          xa[i][0][t] = (u32x4){0u, 0u, 0u, 0u};
+          xb[i][0][t] = (u32x4){0u, 0u, 0u, 0u};
           if constexpr (SCH == kW8A16) {
             if (ok && row_ok)
               load_x_bf16x16<FAST>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)(m0 + r) * a.K, kt * kTileK + g * 16,
-                                   a.K, xa[i][t], xb[i][t]);
+                                   a.K, xa[i][0][t], xb[i][0][t]);
           } else {
             if (ok && row_ok)
-              xa[i][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)(m0 + r) * a.K,
-                                              kt * kTileK + g * 16, a.K);
+              xa[i][0][t] = load_x_codes16<FAST>(reinterpret_cast<const uint8_t*>(a.x) + (int64_t)(m0 + r) * a.K,
+                                                 kt * kTileK + g * 16, a.K);
           }
         }
       }
@@ -273,20 +303,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   }
 
   // ---- sum the waves through LDS (wave c finishes column tile nt + c)
-  __shared__ f32x4 red[CT][NW][64];
+  __shared__ f32x4 red[RW * CT][NW][64];
 #pragma unroll
-  for (int c = 0; c < CT; ++c) red[c][wave][lane] = T::kIntAcc ? __builtin_bit_cast(f32x4, acci[c]) : accf[c];
+  for (int q = 0; q < RW; ++q)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      red[q * CT + c][wave][lane] = T::kIntAcc ? __builtin_bit_cast(f32x4, acci[q][c]) : accf[q][c];
   __syncthreads();
-  if (wave >= CT || nt + wave >= a.NT) return;
+  // wave q * CT + c finishes column tile nt + c of row group rg + q (pairs have CT = 1)
+  if (wave >= RW * CT || (RW == 1 && nt + wave >= a.NT) || (RW == 2 && wave == 1 && rows1 <= 0)) return;
+  const int rq = RW == 1 ? 0 : wave;
   const int cw = CT == 1 ? 0 : wave;
+  const int slot = rq * CT + cw;
   f32x4 tot;
   if constexpr (T::kIntAcc) {
-    i32x4 t = __builtin_bit_cast(i32x4, red[cw][0][lane]);
-    for (int w = 1; w < NW; ++w) t += __builtin_bit_cast(i32x4, red[cw][w][lane]);
+    i32x4 t = __builtin_bit_cast(i32x4, red[slot][0][lane]);
+    for (int w = 1; w < NW; ++w) t += __builtin_bit_cast(i32x4, red[slot][w][lane]);
     tot = __builtin_bit_cast(f32x4, t);
   } else {
-    tot = red[cw][0][lane];
-    for (int w = 1; w < NW; ++w) tot += red[cw][w][lane];
+    tot = red[slot][0][lane];
+    for (int w = 1; w < NW; ++w) tot += red[slot][w][lane];
   }
 
   // ---- split-K (one column tile per workgroup): publish, count arrivals, last one
@@ -294,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   if (CT == 1 && S > 1) {
     const __amdgpu_buffer_rsrc_t part = partial_rsrc(a.partials, a.partials_bytes);
     // partial of (slice, row group, column tile); one counter per (row group, column tile)
-    const int64_t col = RG ? (int64_t)rg * a.NT + nt : nt;
+    const int64_t col = RG ? (int64_t)(rg + rq) * a.NT + nt : nt;
     const int64_t slice = RG ? (int64_t)NRG * a.NT : a.NT;
     store_partial(part, ((int64_t)s * slice + col) * 64 + lane, tot);
     wait_stores_performed();
@@ -328,7 +364,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   if (SCH == kW8A8 && !a.out_acc) sw = a.scale_per_tensor ? a.w_scale[0] : a.w_scale[n];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = m0 + 4 * g + j;
+    const int m = m0 + 16 * rq + 4 * g + j;
     if (m >= a.M) break;
     const int64_t o = (int64_t)m * a.N + n;
     if constexpr (SCH == kW8A16) {
@@ -347,7 +383,13 @@ template <int QT, int SCH, int NW, bool RG>
 hipError_t launch_small_rg(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
   // several row groups: planned for the aligned path only
   if (!a.fast) return hipErrorInvalidValue;
-  if (p.ct == 2)
+  if (p.ct == 1 && p.rw == 2) {
+    // two row groups per workgroup: the weights loaded once for both
+    if constexpr (SCH == kW8A8 && QT == kFp8 && NW == 16) return hipErrorInvalidValue;
+    else gemm_small_kernel<QT, SCH, true, NW, 1, RG, 2><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  } else if (p.rw != 1) {
+    return hipErrorInvalidValue;
+  } else if (p.ct == 2)
     gemm_small_kernel<QT, SCH, true, NW, 2, RG><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
   else if (p.ct == 4)
     gemm_small_kernel<QT, SCH, true, NW, 4, RG><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);

@@ -20,6 +20,7 @@ struct GemmPlan {
   int units_per_wave = 0;   // small-M: K units per wave
   int waves = 4;            // small-M: waves per workgroup (4, 8 or 16)
   int ct = 1;               // small-M: 16-column tiles per workgroup (1, 2 or 4)
+  int rw = 1;               // small-M: 16-row groups per workgroup (1 or 2)
   int BM = 0, BN = 0;       // large-M: workgroup tile
   int tiles = 0;            // output tiles (small: 16-column blocks)
   int grid = 0;             // workgroups launched
