@@ -417,10 +417,12 @@ def test_batched_decode_plans_take_row_groups():
     weights of at most 20M codes (over K <= 8192: 28M, for W8A8 on at most 512 column
     tiles), four for at most 12M (W8A16 over K = 2048: 24M); from 65 to 128 rows narrow
     outputs over K <= 4096 and weights of at most 4M codes on at most 128 column tiles;
-    ragged K and larger M keep the large-M kernels.  Two groups share a workgroup (tile_m
-    32) on weights of at least 128 column tiles over K >= 8192 with one column tile per
-    workgroup.  The grid and workspace count every group, and K slices keep one arrival
-    counter per (group, column tile) inside the counter region."""
+    ragged K and larger M keep the large-M kernels.  With one column tile per workgroup, two
+    groups share a workgroup (tile_m 32) on 192 or more column tiles, or on at least 128
+    over K >= 8192, and three groups take a pair and a single (the pair's second group
+    past M) on fewer than 128 column tiles over K >= 8192.  The grid and workspace count
+    every group, and K slices keep one arrival counter per (group, column tile) inside the
+    counter region."""
     def cdiv(a, b):
         return -(-a // b)
 
@@ -449,7 +451,8 @@ def test_batched_decode_plans_take_row_groups():
                         if p["kind"] != 0:
                             continue
                         NT, ct, S, rw = cdiv(N, 16), p["tile_n"] // 16, p["split_k"], p["tile_m"] // 16
-                        pair = nrg == 2 and ct == 1 and K >= 8192 and NT >= 128
+                        pair = ct == 1 and ((nrg == 2 and (NT >= 192 or (K >= 8192 and NT >= 128))) or
+                                            (nrg == 3 and NT < 128 and K >= 8192))
                         if sch != "w8a16" and qt == "fp8_e4m3fn" and p["waves"] == 16:
                             pair = False                  # no 16-wave FP8 W8A8 pair build
                         assert rw == (2 if pair else 1), where

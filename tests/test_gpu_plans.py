@@ -1,7 +1,7 @@
 """Parity of every launch plan the planner chooses (large M: tile configuration, split or
 not; small M: waves per workgroup, 16-column tiles per workgroup, split or not, aligned
-K or not, one or several 16-row groups), beyond the ones the small shapes of
-test_gpu_gemm.py reach.
+K or not, one or several 16-row groups, one or two of them per workgroup), beyond the
+ones the small shapes of test_gpu_gemm.py reach.
 
 The direct-to-LDS kernel has one instantiation per tile configuration, and the
 loop of each differs (waves per tile, stages, whether a wave copies exactly the
@@ -67,8 +67,10 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      (17, 4544, 1014), (17, 4096, 2385), (20, 6464, 16),    # K slices, 4 / 8 waves
                      (100, 1024, 500), (128, 4096, 100),                    # narrow: 7 and 8 groups
                      (80, 1024, 2048),                                      # 128 column tiles, 5 groups
-                     # two row groups per workgroup (deep weights): K slices or not, 4 to 16 waves
-                     (17, 8576, 2385), (17, 8576, 3299), (17, 8576, 4213)]
+                     # two row groups per workgroup (deep or wide weights): K slices or not, 4 to
+                     # 16 waves; three groups (the second pair's second group past M)
+                     (17, 8576, 2385), (17, 8576, 3299), (17, 8576, 4213), (17, 64, 3299),
+                     (33, 8384, 16), (33, 8384, 413), (33, 8384, 1604)]
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

@@ -304,14 +304,21 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
       // faster than eight in the third sweep.
       if (ct == 1 && S == 1 && TPU == 2 && NT >= 256 && KU >= 64) W = 4;
     }
-    // Two row groups per workgroup (each unit's weights loaded once for both) on deep
-    // weights with one column tile: same-box timings at M = 17 / 24 / 32 over 8192 and
-    // 11008 inputs to 2048 and 4096 outputs, all three schemes, 0.61-0.83 / 0.69-0.92 /
-    // 0.78-0.99 of the time with one group per workgroup (11008 -> 4096 INT8 W8A16 at
-    // M = 17: 26.7 -> 16.7 us); on shallower or narrower weights the halved grid lost
-    // (2048 x 2048 at M = 24: 1.12-1.19x; 14336 -> 1024: 1.18-1.25x).
+    // Two row groups per workgroup (each unit's weights loaded once for both) with one
+    // column tile, where the halved grid still fills the chip.  Same-box timings against
+    // one group per workgroup, all three schemes: two groups over K >= 8192 on at least
+    // 128 column tiles (8192 and 11008 inputs to 2048 and 4096 outputs) 0.61-0.83 /
+    // 0.69-0.92 / 0.78-0.99 of the time at M = 17 / 24 / 32 (11008 -> 4096 INT8 W8A16 at
+    // M = 17: 26.7 -> 16.7 us), on 192 or more column tiles at any depth 0.66-0.98
+    // (6144 -> 4096 INT8 W8A16 at M = 17: 0.66); three groups on narrow outputs over
+    // K >= 8192 0.78-0.96 at M = 40 / 48 (M = 33, one row in the third group: 0.81-1.05).
+    // Elsewhere the halved grid lost (2048 x 2048 at M = 24: 1.12-1.19x; 14336 -> 1024
+    // with two groups: 1.18-1.25x; wide outputs with three groups: 1.07-1.21x).
     int64_t rw = 1;
-    if (NRG == 2 && ct == 1 && fast && K >= 8192 && NT >= 128 && !(TPU == 2 && W == 16)) rw = 2;   // no 16-wave FP8 W8A8 pair build
+    if (ct == 1 && fast && !(TPU == 2 && W == 16)) {   // no 16-wave FP8 W8A8 pair build
+      if (NRG == 2 && (NT >= 192 || (K >= 8192 && NT >= 128))) rw = 2;
+      else if (NRG == 3 && NT < 128 && K >= 8192) rw = 2;
+    }
     // One arrival counter per (row group, column tile): NRG <= 4 keeps every split plan
     // above (fewer than 192 column tiles, or one row group) within the counter region.
     if (S > 1 && NT * NRG > kMaxSplitTiles) {
