@@ -420,7 +420,8 @@ def test_batched_decode_plans_take_row_groups():
     ragged K and larger M keep the large-M kernels.  With one column tile per workgroup, two
     groups share a workgroup (tile_m 32) on 192 or more column tiles, or on at least 128
     over K >= 8192, and three groups take a pair and a single (the pair's second group
-    past M) on fewer than 128 column tiles over K >= 8192.  The grid and workspace count
+    past M) on fewer than 128 column tiles over K >= 8192; on exactly 128 column tiles over
+    K >= 8192 three groups take one workgroup of four (tile_m 64).  The grid and workspace count
     every group, and K slices keep one arrival counter per (group, column tile) inside the
     counter region."""
     def cdiv(a, b):
@@ -436,7 +437,8 @@ def test_batched_decode_plans_take_row_groups():
                         nrg = cdiv(M, 16)
                         w16 = sch == "w8a16"
                         by_size = {3: N * K <= 20 << 20 or (K <= 8192 and N * K <= 28 << 20 and
-                                                              (w16 or cdiv(N, 16) <= 512)),
+                                                              (w16 or cdiv(N, 16) <= 512)) or
+                                      (K >= 8192 and cdiv(N, 16) == 128),
                                    4: N * K <= 12 << 20 or (w16 and K <= 2048 and N * K <= 24 << 20)}
                         narrow = cdiv(N, 16) < 128
                         if M <= 16:
@@ -455,7 +457,9 @@ def test_batched_decode_plans_take_row_groups():
                                             (nrg == 3 and NT < 128 and K >= 8192))
                         if sch != "w8a16" and qt == "fp8_e4m3fn" and p["waves"] == 16:
                             pair = False                  # no 16-wave FP8 W8A8 pair build
-                        assert rw == (2 if pair else 1), where
+                        quad = nrg == 3 and K >= 8192 and NT == 128
+                        assert ct == 1 or not quad, where
+                        assert rw == (4 if quad else 2 if pair else 1), where
                         assert p["grid"] == cdiv(NT, ct) * S * cdiv(nrg, rw), where
                         if S > 1:
                             assert NT * nrg <= 1024 and p["workspace_bytes"] >= S * nrg * NT * 1024, where

@@ -193,7 +193,8 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     else if (groups <= 2) small = K < 12288;
     else if (groups == 3)
       small = N * K <= (int64_t(20) << 20) ||
-              (K <= 8192 && N * K <= (int64_t(28) << 20) && (scheme == kW8A16 || NT <= 512));
+              (K <= 8192 && N * K <= (int64_t(28) << 20) && (scheme == kW8A16 || NT <= 512)) ||
+              (K >= 8192 && NT == 128);   // four groups per workgroup, see below
     else small = N * K <= (int64_t(12) << 20) || (scheme == kW8A16 && K <= 2048 && N * K <= (int64_t(24) << 20));
   }
   if (!small && aligned_path) return plan_mfma(scheme, M, K, N);
@@ -225,9 +226,20 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // W8A8) / 4 % (FP8 W8A8) faster than the first rule alone.
     p.kind = 0;
     // Above 16 rows every 16-row group is a workgroup of its own: the rules below see
-    // a group's rows (Mg) and count workgroups and waves over all NRG groups.
+    // a group's rows (Mg) and count workgroups and waves over all NRG groups (NRW
+    // workgroups per column tile and slice).  Three groups over K >= 8192 on exactly
+    // 128 column tiles take one workgroup of four groups instead (each unit's weights
+    // loaded once for all of them; the fourth group lies past M): two K slices then make
+    // one workgroup per CU.  Same-box timings against the plans before (three single
+    // groups up to 20M weight codes, the direct-to-LDS kernel above) at M = 33 / 40 / 48
+    // over K = 8192 to 16384 to 2048 outputs: INT8 W8A16 0.73-1.05 of the time (11008 ->
+    // 2048 at M = 33: 24.4 -> 18.7 us), FP8 W8A8 0.74-0.92, INT8 W8A8 0.79-0.98.  With
+    // 138 to 188 column tiles the 276 to 376 workgroups take a second round on part of
+    // the CUs (1.01-1.79x), and wider outputs, shallower weights and M = 64 lost too.
     const int64_t Mg = std::min<int64_t>(M, 16), NRG = cdiv(M, 16);
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
+    const bool quad = NRG == 3 && fast && K >= 8192 && NT == 128;
+    const int64_t NRW = quad ? 1 : NRG;
     const int64_t KU = cdiv(KT, TPU);
     const int64_t max_waves = TPU == 2 ? 8 : 16;
     // A third sweep (N 1024 to 8192 with K 4096 to 28672, M 1 / 4 / 8 / 16, every
@@ -243,7 +255,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     int64_t S = 1;
     const bool narrow = NT < 128 && fast;
     const int64_t narrow_units = TPU == 2 ? 48 : (scheme == kW8A16 && Mg > 8 ? 32 : 64);
-    if (narrow) S = std::max<int64_t>(1, std::min(cdiv(256, NT * NRG), cdiv(KU, narrow_units)));
+    if (narrow) S = std::max<int64_t>(1, std::min(cdiv(256, NT * NRW), cdiv(KU, narrow_units)));
     else if (NT < 128) S = std::min(cdiv(128, NT), std::max<int64_t>(1, KU / kSmallUnitsPerWave));
     else if (NT < 192 && KU >= 64) S = 2;
     int64_t ups = cdiv(KU, S);
@@ -251,11 +263,11 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     int64_t W = 4;
     while (W < max_waves && cdiv(ups, W) > kSmallUnitsPerWave) W *= 2;
     if (!narrow)
-      while (W < max_waves && NT * NRG * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
+      while (W < max_waves && NT * NRW * S * W <= (TPU == 2 ? 256 : 512)) W *= 2;
     int64_t ct = 1;
     if (S == 1) {
       const int64_t cap = scheme == kW8A16 ? 12 : 24;           // waves per CU
-      while (W > 4 && NT * NRG * W > cap * 256) W /= 2;
+      while (W > 4 && NT * NRW * W > cap * 256) W /= 2;
       const int64_t m2 = scheme == kW8A16 ? 6 : 12;                      // rows for two tiles
       const int64_t m4 = scheme == kW8A16 ? 8 : (TPU == 2 ? 12 : Mg + 1);  // rows for four
       // With 4096 <= K < 8192, two tiles at any M (each unit's x loads then serve
@@ -269,16 +281,16 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
         const double r = (double)g / 256.0;
         return std::ceil(r) / r;
       };
-      const bool k_mid = K >= 4096 && K < 8192 && spread(cdiv(NT, 2) * NRG) <= spread(NT * NRG) + 1e-9;
-      if (fast && Mg >= m4 && NT >= 640) ct = 4;
-      else if (fast && (Mg >= m2 || k_mid) && NT >= 320) ct = 2;
+      const bool k_mid = K >= 4096 && K < 8192 && spread(cdiv(NT, 2) * NRW) <= spread(NT * NRW) + 1e-9;
+      if (!quad && fast && Mg >= m4 && NT >= 640) ct = 4;
+      else if (!quad && fast && (Mg >= m2 || k_mid) && NT >= 320) ct = 2;
       if (ct > 1) {
         const int64_t groups = cdiv(NT, ct);
         const int64_t w_max = (ct == 2 && scheme == kW8A8) ? 8 : 16;
         double best = 1e300;
         for (int64_t w = 4; w <= w_max; w *= 2) {
           if (w > 4 && w > KU) break;
-          const double d = std::fabs((double)(groups * NRG * w) / 256.0 - 14.0);
+          const double d = std::fabs((double)(groups * NRW * w) / 256.0 - 14.0);
           if (d < best - 1e-9) {
             best = d;
             W = w;
@@ -291,7 +303,7 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
       // The third sweep: 320 and 384 column tiles over K = 8192 to 14336 at M <= 8,
       // 5-15 % faster (13824 -> 5120, 14336 -> 6144); shallower weights on the same
       // tile counts gained nothing.
-      if (ct == 1 && NRG == 1 && NT > 256 && NT <= kMaxSplitTiles && KU >= (TPU == 2 ? 96 : 128) && spread(NT) > 1.2 + 1e-9) {
+      if (ct == 1 && NRW == 1 && NT > 256 && NT <= kMaxSplitTiles && KU >= (TPU == 2 ? 96 : 128) && spread(NT) > 1.2 + 1e-9) {
         int64_t s_best = 2;
         for (int64_t s = 3; s <= 4; ++s)
           if (spread(NT * s) < spread(NT * s_best) - 1e-9) s_best = s;
@@ -311,12 +323,14 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // 0.69-0.92 / 0.78-0.99 of the time at M = 17 / 24 / 32 (11008 -> 4096 INT8 W8A16 at
     // M = 17: 26.7 -> 16.7 us), on 192 or more column tiles at any depth 0.66-0.98
     // (6144 -> 4096 INT8 W8A16 at M = 17: 0.66); three groups on narrow outputs over
-    // K >= 8192 0.78-0.96 at M = 40 / 48 (M = 33, one row in the third group: 0.81-1.05).
+    // K >= 8192 0.78-1.00 at M = 40 / 48 (M = 33, one row in the third group: 0.81-1.05).
     // Elsewhere the halved grid lost (2048 x 2048 at M = 24: 1.12-1.19x; 14336 -> 1024
-    // with two groups: 1.18-1.25x; wide outputs with three groups: 1.07-1.21x).
+    // with two groups: 1.06-1.43x; wide outputs with three groups: 1.03-1.21x).
     int64_t rw = 1;
+    if (quad && TPU == 2 && W == 16) W = 8;            // no 16-wave FP8 W8A8 build of several groups
     if (ct == 1 && fast && !(TPU == 2 && W == 16)) {   // no 16-wave FP8 W8A8 pair build
-      if (NRG == 2 && (NT >= 192 || (K >= 8192 && NT >= 128))) rw = 2;
+      if (quad) rw = 4;
+      else if (NRG == 2 && (NT >= 192 || (K >= 8192 && NT >= 128))) rw = 2;
       else if (NRG == 3 && NT < 128 && K >= 8192) rw = 2;
     }
     // One arrival counter per (row group, column tile): NRG <= 4 keeps every split plan

@@ -89,8 +89,8 @@ __device__ __forceinline__ u32x4 load_x_codes16(const uint8_t* row, int k, int K
 // registers its longer units take and runs three.
 // RG: several 16-row groups (M > 16; aligned path).  A separate build, so that the
 // single-group kernel keeps its code: the group arithmetic cost it 2-6 %.
-// RW: row groups per workgroup (1 or 2; 2 with one column tile).  Each unit's weights
-// then serve both groups (one load, two MFMAs), and a load batch holds 8 / (CT RW) units
+// RW: row groups per workgroup (1, 2 or 4; more than one with one column tile).  Each unit's
+// weights then serve every group (one load, RW MFMAs), and a load batch holds 8 / (CT RW) units
 // so the registers in flight stay those of eight single-group units.
 template <int QT, int SCH, bool FAST, int NW, int CT = 1, bool RG = false, int RW = 1>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   using T = SmallTraits<QT, SCH>;
   constexpr int TPU = T::kTilesPerUnit;
   constexpr int kU = kUnroll / (CT * RW);                  // units per load batch
-  static_assert(RW == 1 || (RG && CT == 1), "row-group pairs: one column tile");
+  static_assert(RW == 1 || ((RW == 2 || RW == 4) && RG && CT == 1), "several row groups per workgroup: one column tile");
   static_assert(CT == 1 || ((CT == 2 || CT == 4) && FAST), "several column tiles on the aligned path only");
   static_assert(!RG || FAST, "several row groups on the aligned path only");
   // The wave index is uniform across the wave: reading it once keeps the unit range and
@@ -128,8 +128,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
   // Rows of the second group of a pair (0 when the pair's first group is the last one).
   // Uniform; the clamp compiles to a vector instruction, so it is read back into a
   // scalar register for the buffer descriptor built from it.
-  const int left1 = a.M - m0 - 16;
-  const int rows1 = RW == 2 ? __builtin_amdgcn_readfirstlane(left1 < 0 ? 0 : (left1 < 16 ? left1 : 16)) : 0;
+  auto rows_of = [&](int q) {
+    const int left = a.M - m0 - 16 * q;
+    return __builtin_amdgcn_readfirstlane(left < 0 ? 0 : (left < 16 ? left : 16));
+  };
+  const int rows1 = RW >= 2 ? rows_of(1) : 0;
+  const int rows2 = RW == 4 ? rows_of(2) : 0;
+  const int rows3 = RW == 4 ? rows_of(3) : 0;
   const int KU = (a.KT + TPU - 1) / TPU;
   const int u_begin = s * ups + wave * upw;
   int u_end = u_begin + upw;
@@ -205,10 +210,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
     // Second group of a pair: named values rather than arrays, which the compiler
     // keeps in vector registers (every load then loops over the lanes' descriptors).
     // A group past the last row has an empty range: its loads return zeros.
-    const __amdgpu_buffer_rsrc_t xrs1 = RW == 1 ? xrs : __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.x)) + (int64_t)(m0 + 16) * a.K * kEsz, 0,
-        rows1 * a.K * kEsz, kBufferWord3);
+    auto x_rsrc = [&](int q, int rq_rows) {
+      return __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.x)) + (int64_t)(m0 + 16 * q) * a.K * kEsz, 0,
+          rq_rows * a.K * kEsz, kBufferWord3);
+    };
+    const __amdgpu_buffer_rsrc_t xrs1 = RW == 1 ? xrs : x_rsrc(1, rows1);
+    const __amdgpu_buffer_rsrc_t xrs2 = RW < 4 ? xrs : x_rsrc(2, rows2);
+    const __amdgpu_buffer_rsrc_t xrs3 = RW < 4 ? xrs : x_rsrc(3, rows3);
     const uint32_t xrow1 = r < rows1 ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
+    const uint32_t xrow2 = r < rows2 ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
+    const uint32_t xrow3 = r < rows3 ? (uint32_t)((r * a.K + g * 16) * kEsz) : 0x80000000u;
     auto run = [&](int u0, auto nu) {
       constexpr int NU = decltype(nu)::value;
       u32x4 wv[NU][CT][TPU], xa[NU][RW][TPU], xb[NU][RW][TPU];
@@ -226,11 +238,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
           xa[i][0][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0);
           xb[i][0][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(xo + 16), 0, 0)
                                       : (u32x4){0u, 0u, 0u, 0u};
-          if constexpr (RW == 2) {
-            const uint32_t xo1 = kt_in ? xrow1 + (uint32_t)(kt * kTileK * kEsz) : 0x80000000u;
-            xa[i][1][t] = __builtin_amdgcn_raw_buffer_load_b128(xrs1, (int)xo1, 0, 0);
-            xb[i][1][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(xrs1, (int)(xo1 + 16), 0, 0)
+          auto load_x = [&](int q, __amdgpu_buffer_rsrc_t rs, uint32_t xr) {
+            const uint32_t xq = kt_in ? xr + (uint32_t)(kt * kTileK * kEsz) : 0x80000000u;
+            xa[i][q][t] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)xq, 0, 0);
+            xb[i][q][t] = SCH == kW8A16 ? __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(xq + 16), 0, 0)
                                         : (u32x4){0u, 0u, 0u, 0u};
+          };
+          if constexpr (RW >= 2) load_x(1, xrs1, xrow1);
+          if constexpr (RW == 4) {
+            load_x(2, xrs2, xrow2);
+            load_x(3, xrs3, xrow3);
           }
         }
         __builtin_amdgcn_sched_barrier(0);   // issue order = unit order
@@ -311,7 +328,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(
       red[q * CT + c][wave][lane] = T::kIntAcc ? __builtin_bit_cast(f32x4, acci[q][c]) : accf[q][c];
   __syncthreads();
   // wave q * CT + c finishes column tile nt + c of row group rg + q (pairs have CT = 1)
+  // (a group past M has nothing to finish)
   if (wave >= RW * CT || (RW == 1 && nt + wave >= a.NT) || (RW == 2 && wave == 1 && rows1 <= 0)) return;
+  if (RW == 4 && wave > 0 && (wave == 1 ? rows1 : wave == 2 ? rows2 : rows3) <= 0) return;
   const int rq = RW == 1 ? 0 : wave;
   const int cw = CT == 1 ? 0 : wave;
   const int slot = rq * CT + cw;
@@ -387,6 +406,10 @@ hipError_t launch_small_rg(const GemmPlan& p, const GemmArgs& a, hipStream_t st)
     // two row groups per workgroup: the weights loaded once for both
     if constexpr (SCH == kW8A8 && QT == kFp8 && NW == 16) return hipErrorInvalidValue;
     else gemm_small_kernel<QT, SCH, true, NW, 1, RG, 2><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
+  } else if (p.ct == 1 && p.rw == 4) {
+    // four row groups per workgroup
+    if constexpr (SCH == kW8A8 && QT == kFp8 && NW == 16) return hipErrorInvalidValue;
+    else gemm_small_kernel<QT, SCH, true, NW, 1, RG, 4><<<p.grid, NW * 64, 0, st>>>(a, p.S, p.units_per_split, p.units_per_wave);
   } else if (p.rw != 1) {
     return hipErrorInvalidValue;
   } else if (p.ct == 2)
