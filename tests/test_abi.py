@@ -421,7 +421,8 @@ def test_batched_decode_plans_take_row_groups():
     groups share a workgroup (tile_m 32) on 192 or more column tiles, or on at least 128
     over K >= 8192, and three groups take a pair and a single (the pair's second group
     past M) on fewer than 128 column tiles over K >= 8192; on exactly 128 column tiles over
-    K >= 8192 three groups take one workgroup of four (tile_m 64).  The grid and workspace count
+    K >= 8192, and on 64 column tiles over K >= 14336 (FP8 W8A8: K >= 28672), three groups
+    take one workgroup of four (tile_m 64).  The grid and workspace count
     every group, and K slices keep one arrival counter per (group, column tile) inside the
     counter region."""
     def cdiv(a, b):
@@ -430,8 +431,8 @@ def test_batched_decode_plans_take_row_groups():
     for sch in ("w8a16", "w8a8_static"):
         for qt in ("int8", "fp8_e4m3fn"):
             for M in (16, 17, 24, 32, 33, 48, 64, 65, 100, 128, 129):
-                for K in (64, 1000, 2048, 3072, 4096, 8192, 11008, 12288, 14336):
-                    for N in (16, 1024, 2048, 4096, 5632, 8192, 11008):
+                for K in (64, 1000, 2048, 3072, 4096, 8192, 11008, 12288, 14336, 28672):
+                    for N in (16, 1000, 1024, 2048, 4096, 5632, 8192, 11008):
                         p = qlq.gemm_plan(sch, M, K, N, qt)
                         where = (sch, qt, M, K, N, p)
                         nrg = cdiv(M, 16)
@@ -457,7 +458,9 @@ def test_batched_decode_plans_take_row_groups():
                                             (nrg == 3 and NT < 128 and K >= 8192))
                         if sch != "w8a16" and qt == "fp8_e4m3fn" and p["waves"] == 16:
                             pair = False                  # no 16-wave FP8 W8A8 pair build
-                        quad = nrg == 3 and K >= 8192 and NT == 128
+                        fp8_w8a8 = sch != "w8a16" and qt == "fp8_e4m3fn"
+                        quad = nrg == 3 and ((K >= 8192 and NT == 128) or
+                                             (NT == 64 and K >= 14336 and (not fp8_w8a8 or K >= 28672)))
                         assert ct == 1 or not quad, where
                         assert rw == (4 if quad else 2 if pair else 1), where
                         assert p["grid"] == cdiv(NT, ct) * S * cdiv(nrg, rw), where

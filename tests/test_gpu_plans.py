@@ -71,8 +71,10 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      # 16 waves; three groups (the second pair's second group past M)
                      (17, 8576, 2385), (17, 8576, 3299), (17, 8576, 4213), (17, 64, 3299),
                      (33, 8384, 16), (33, 8384, 413), (33, 8384, 1604),
-                     # three groups in one workgroup of four (deep weights, 128 column tiles)
-                     (33, 8384, 2047), (47, 8192, 2040), (40, 16384, 2048)]
+                     # three groups in one workgroup of four (deep weights, 128 column tiles;
+                     # 64 column tiles over deeper weights, with K slices)
+                     (33, 8384, 2047), (47, 8192, 2040), (40, 16384, 2048),
+                     (35, 14336, 1010), (48, 28672, 1024)]
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

@@ -236,9 +236,15 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // 2048 at M = 33: 24.4 -> 18.7 us), FP8 W8A8 0.74-0.92, INT8 W8A8 0.79-0.98.  With
     // 138 to 188 column tiles the 276 to 376 workgroups take a second round on part of
     // the CUs (1.01-1.79x), and wider outputs, shallower weights and M = 64 lost too.
+    // Narrow outputs of 64 column tiles (1024 outputs) over K >= 14336 take the same
+    // workgroup of four groups (K slices up to 256 workgroups) in place of a pair and a
+    // single: 14336 / 16384 -> 1024 INT8 W8A16 0.82-0.94, INT8 W8A8 0.82-0.94, FP8 W8A8
+    // 0.94-1.07 (so FP8 W8A8 only from K = 28672), 28672 -> 1024 0.75-0.89 in all three.
+    // 32 and 96 column tiles, and 64 over K = 8192, lost (up to 1.3x).
     const int64_t Mg = std::min<int64_t>(M, 16), NRG = cdiv(M, 16);
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
-    const bool quad = NRG == 3 && fast && K >= 8192 && NT == 128;
+    const bool quad = NRG == 3 && fast &&
+                      ((K >= 8192 && NT == 128) || (NT == 64 && K >= 14336 && (TPU == 1 || K >= 28672)));
     const int64_t NRW = quad ? 1 : NRG;
     const int64_t KU = cdiv(KT, TPU);
     const int64_t max_waves = TPU == 2 ? 8 : 16;
