@@ -421,8 +421,9 @@ def test_batched_decode_plans_take_row_groups():
     groups share a workgroup (tile_m 32) on 192 or more column tiles, or on at least 128
     over K >= 8192, and three groups take a pair and a single (the pair's second group
     past M) on fewer than 128 column tiles over K >= 8192; on exactly 128 column tiles over
-    K >= 8192, and on 64 column tiles over K >= 14336 (FP8 W8A8: K >= 28672), three groups
-    take one workgroup of four (tile_m 64).  The grid and workspace count
+    K >= 8192, on 64 column tiles over K >= 14336 (FP8 W8A8: K >= 28672) and, in W8A8, on 80
+    to 127 column tiles over K >= 8192 (FP8 up to 24M weight codes, INT8 below K = 10240),
+    three groups take one workgroup of four (tile_m 64).  The grid and workspace count
     every group, and K slices keep one arrival counter per (group, column tile) inside the
     counter region."""
     def cdiv(a, b):
@@ -432,7 +433,7 @@ def test_batched_decode_plans_take_row_groups():
         for qt in ("int8", "fp8_e4m3fn"):
             for M in (16, 17, 24, 32, 33, 48, 64, 65, 100, 128, 129):
                 for K in (64, 1000, 2048, 3072, 4096, 8192, 11008, 12288, 14336, 28672):
-                    for N in (16, 1000, 1024, 2048, 4096, 5632, 8192, 11008):
+                    for N in (16, 1000, 1024, 1536, 2048, 4096, 5632, 8192, 11008):
                         p = qlq.gemm_plan(sch, M, K, N, qt)
                         where = (sch, qt, M, K, N, p)
                         nrg = cdiv(M, 16)
@@ -460,7 +461,9 @@ def test_batched_decode_plans_take_row_groups():
                             pair = False                  # no 16-wave FP8 W8A8 pair build
                         fp8_w8a8 = sch != "w8a16" and qt == "fp8_e4m3fn"
                         quad = nrg == 3 and ((K >= 8192 and NT == 128) or
-                                             (NT == 64 and K >= 14336 and (not fp8_w8a8 or K >= 28672)))
+                                             (NT == 64 and K >= 14336 and (not fp8_w8a8 or K >= 28672)) or
+                                             (sch != "w8a16" and 80 <= NT < 128 and K >= 8192 and
+                                              (N * K <= 24 << 20 if fp8_w8a8 else K < 10240)))
                         assert ct == 1 or not quad, where
                         assert rw == (4 if quad else 2 if pair else 1), where
                         assert p["grid"] == cdiv(NT, ct) * S * cdiv(nrg, rw), where

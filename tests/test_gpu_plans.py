@@ -74,7 +74,7 @@ SMALL_PLAN_SHAPES = [(3, 2624, 413),     # four waves, K slices, aligned K
                      # three groups in one workgroup of four (deep weights, 128 column tiles;
                      # 64 column tiles over deeper weights, with K slices)
                      (33, 8384, 2047), (47, 8192, 2040), (40, 16384, 2048),
-                     (35, 14336, 1010), (48, 28672, 1024)]
+                     (35, 14336, 1010), (48, 28672, 1024), (40, 8192, 1500), (47, 12288, 1920)]
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

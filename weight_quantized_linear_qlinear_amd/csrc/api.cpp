@@ -240,11 +240,16 @@ GemmPlan plan_gemm(int scheme, int qtype, int64_t M, int64_t K, int64_t N, bool 
     // workgroup of four groups (K slices up to 256 workgroups) in place of a pair and a
     // single: 14336 / 16384 -> 1024 INT8 W8A16 0.82-0.94, INT8 W8A8 0.82-0.94, FP8 W8A8
     // 0.94-1.07 (so FP8 W8A8 only from K = 28672), 28672 -> 1024 0.75-0.89 in all three.
-    // 32 and 96 column tiles, and 64 over K = 8192, lost (up to 1.3x).
+    // 32 and 96 column tiles, and 64 over K = 8192, lost (up to 1.3x), except in W8A8:
+    // on 80 to 127 column tiles FP8 W8A8 took 0.62-0.99 of the time over K = 8192 to 14336
+    // up to 24M weight codes (14336 -> 1920: 0.95-1.13), INT8 W8A8 0.83-0.98 over K = 8192
+    // (deeper, at M = 40 / 48: up to 1.19x).
     const int64_t Mg = std::min<int64_t>(M, 16), NRG = cdiv(M, 16);
     const int64_t TPU = (scheme == kW8A8 && qtype == 1) ? 2 : 1;
     const bool quad = NRG == 3 && fast &&
-                      ((K >= 8192 && NT == 128) || (NT == 64 && K >= 14336 && (TPU == 1 || K >= 28672)));
+                      ((K >= 8192 && NT == 128) || (NT == 64 && K >= 14336 && (TPU == 1 || K >= 28672)) ||
+                       (scheme == kW8A8 && NT >= 80 && NT < 128 && K >= 8192 &&
+                        (TPU == 2 ? N * K <= (int64_t(24) << 20) : K < 10240)));
     const int64_t NRW = quad ? 1 : NRG;
     const int64_t KU = cdiv(KT, TPU);
     const int64_t max_waves = TPU == 2 ? 8 : 16;
